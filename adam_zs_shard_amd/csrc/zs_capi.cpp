@@ -1,0 +1,454 @@
+// zs_capi.cpp -- the C ABI of libzshard: argument checks, the shard plan, the
+// fp32 constants, the alignment head, and the calls into the HIP launchers.
+// Every argument error is returned before anything touches the device.
+
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "../../include/zshard.h"
+#include "zs_internal.h"
+
+static_assert(ZS_MAX_P == zs::kMaxP, "ZS_MAX_P and the kernel table size must agree");
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+zs_status hip_fail(hipError_t e) {
+  g_last_hip_error = static_cast<int32_t>(e);
+  return ZS_ERR_HIP;
+}
+
+bool dtype_ok(int32_t dt) { return dt == ZS_F16 || dt == ZS_BF16; }
+
+// Largest n accepted: keeps every byte offset (4 * n) far inside int64.
+constexpr int64_t kMaxN = int64_t{1} << 60;
+
+zs_status check_hparams(const zs_adam_hparams* hp) {
+  if (!hp) return ZS_ERR_NULL;
+  if (!std::isfinite(hp->lr) || !std::isfinite(hp->eps)) return ZS_ERR_ARG;
+  if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0)) return ZS_ERR_ARG;
+  if (!(hp->beta2 >= 0.0 && hp->beta2 < 1.0)) return ZS_ERR_ARG;
+  if (hp->step < 1) return ZS_ERR_ARG;
+  if (hp->form != ZS_ADAM_STANDARD && hp->form != ZS_ADAM_PAGE1_LITERAL) return ZS_ERR_ARG;
+  if (hp->reserved != 0) return ZS_ERR_ARG;
+  return ZS_OK;
+}
+
+// fp32 constants of one step: each computed in double and rounded once.
+zs::Consts make_consts(const zs_adam_hparams& hp, int32_t p) {
+  zs::Consts c;
+  const double t = static_cast<double>(hp.step);
+  c.B1 = static_cast<float>(hp.beta1);
+  c.C1 = static_cast<float>(1.0 - hp.beta1);
+  c.B2 = static_cast<float>(hp.beta2);
+  c.C2 = static_cast<float>(1.0 - hp.beta2);
+  c.BC1 = static_cast<float>(1.0 - std::pow(hp.beta1, t));
+  c.BC2 = static_cast<float>(1.0 - std::pow(hp.beta2, t));
+  c.LR = static_cast<float>(hp.lr);
+  c.EPS = static_cast<float>(hp.eps);
+  c.PF = static_cast<float>(static_cast<double>(p));
+  return c;
+}
+
+// M = ceil(n/p); rank k: [min(kM, n), min((k+1)M, n)).
+void shard_bounds(int64_t n, int32_t p, int32_t k, int64_t* m, int64_t* s, int64_t* e) {
+  const int64_t mm = n / p + (n % p != 0 ? 1 : 0);
+  const int64_t lo = static_cast<int64_t>(k) * mm;
+  const int64_t hi = lo + mm;
+  *m = mm;
+  *s = lo < n ? lo : n;
+  *e = hi < n ? hi : n;
+}
+
+struct Range {
+  uintptr_t lo, hi;
+};
+bool overlap(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Elements to peel so that as many bytes per element as possible start each
+// 8-element group on a 16-byte boundary.  16-bit streams weigh 2 bytes each
+// (gradients read, the working copy written); fp32 state arrays weigh 8
+// (read and written).
+int choose_head(const std::vector<uintptr_t>& a16, const std::vector<uintptr_t>& a32) {
+  int best = 0, best_score = -1;
+  for (int h = 0; h < zs::kVec; ++h) {
+    int score = 0;
+    for (uintptr_t a : a16) score += ((a + 2u * h) % 16u == 0) ? 2 : 0;
+    for (uintptr_t a : a32) score += ((a + 4u * h) % 16u == 0) ? 8 : 0;
+    if (score > best_score) {
+      best_score = score;
+      best = h;
+    }
+  }
+  return best;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* zs_status_string(int32_t status) {
+  switch (status) {
+    case ZS_OK: return "ZS_OK";
+    case ZS_ERR_NULL: return "ZS_ERR_NULL";
+    case ZS_ERR_ARG: return "ZS_ERR_ARG";
+    case ZS_ERR_DTYPE: return "ZS_ERR_DTYPE";
+    case ZS_ERR_RANGE: return "ZS_ERR_RANGE";
+    case ZS_ERR_ALIAS: return "ZS_ERR_ALIAS";
+    case ZS_ERR_CAPACITY: return "ZS_ERR_CAPACITY";
+    case ZS_ERR_HIP: return "ZS_ERR_HIP";
+    default: return "ZS_ERR_UNKNOWN";
+  }
+}
+
+int32_t zs_version(void) { return ZS_VERSION; }
+
+int32_t zs_last_hip_error(void) { return g_last_hip_error; }
+
+zs_status zs_plan_shards(int64_t n, int32_t p, int64_t* m_out, int64_t* starts, int64_t* ends) {
+  if (n < 0 || p < 1) return ZS_ERR_ARG;
+  if (n > kMaxN) return ZS_ERR_RANGE;
+  for (int32_t k = 0; k < p; ++k) {
+    int64_t m, s, e;
+    shard_bounds(n, p, k, &m, &s, &e);
+    if (m_out) *m_out = m;
+    if (starts) starts[k] = s;
+    if (ends) ends[k] = e;
+  }
+  return ZS_OK;
+}
+
+zs_status zs_fused_shard_step(const zs_shard_args* a) {
+  if (!a) return ZS_ERR_NULL;
+  if (a->p < 1 || a->p > ZS_MAX_P || a->k < 0 || a->k >= a->p || a->n < 0) return ZS_ERR_ARG;
+  if (a->n > kMaxN) return ZS_ERR_RANGE;
+  if (!dtype_ok(a->grad_dtype) || !dtype_ok(a->param_dtype)) return ZS_ERR_DTYPE;
+  if (const zs_status st = check_hparams(a->hp)) return st;
+  if (!a->grads) return ZS_ERR_NULL;
+  int64_t m, s, e;
+  shard_bounds(a->n, a->p, a->k, &m, &s, &e);
+  const int64_t len = e - s;
+  if (a->grad_base < 0 || a->grad_base > s || a->param_base < 0 || a->param_base > s)
+    return ZS_ERR_RANGE;
+  if (len == 0) return ZS_OK;
+  if (!a->w || !a->m || !a->v || !a->param) return ZS_ERR_NULL;
+  for (int32_t r = 0; r < a->p; ++r)
+    if (!a->grads[r]) return ZS_ERR_NULL;
+
+  zs::FusedLaunch L;
+  L.p = a->p;
+  L.gdt = a->grad_dtype;
+  L.pdt = a->param_dtype;
+  L.form = a->hp->form;
+  L.w = a->w;
+  L.m = a->m;
+  L.v = a->v;
+  L.param = static_cast<uint16_t*>(a->param) + (s - a->param_base);
+  L.len = len;
+  L.c = make_consts(*a->hp, a->p);
+  L.stream = static_cast<hipStream_t>(a->stream);
+
+  std::vector<uintptr_t> a16, a32;
+  std::vector<Range> reads;
+  for (int32_t r = 0; r < a->p; ++r) {
+    L.grads[r] = static_cast<const uint16_t*>(a->grads[r]) + (s - a->grad_base);
+    const uintptr_t g0 = reinterpret_cast<uintptr_t>(L.grads[r]);
+    reads.push_back({g0, g0 + 2u * static_cast<uintptr_t>(len)});
+    a16.push_back(g0);
+  }
+  const uintptr_t pw = reinterpret_cast<uintptr_t>(L.w), pm = reinterpret_cast<uintptr_t>(L.m),
+                  pv = reinterpret_cast<uintptr_t>(L.v),
+                  pp = reinterpret_cast<uintptr_t>(L.param);
+  const uintptr_t b32 = 4u * static_cast<uintptr_t>(len), b16 = 2u * static_cast<uintptr_t>(len);
+  const Range writes[4] = {{pw, pw + b32}, {pm, pm + b32}, {pv, pv + b32}, {pp, pp + b16}};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(writes[i], writes[j])) return ZS_ERR_ALIAS;
+    for (const Range& rd : reads)
+      if (overlap(writes[i], rd)) return ZS_ERR_ALIAS;
+  }
+  a16.push_back(pp);
+  a32 = {pw, pm, pv};
+  L.head = choose_head(a16, a32);
+
+  const hipError_t err = zs::launch_fused(L);
+  if (err != hipSuccess) return hip_fail(err);
+  return ZS_OK;
+}
+
+zs_status zs_reduce_scatter_mean_local(const void* const* grads, int32_t grad_dtype,
+                                       int64_t grad_base, int64_t n, int32_t p, int32_t k,
+                                       float* g_out, void* stream) {
+  if (p < 1 || p > ZS_MAX_P || k < 0 || k >= p || n < 0) return ZS_ERR_ARG;
+  if (n > kMaxN) return ZS_ERR_RANGE;
+  if (!dtype_ok(grad_dtype)) return ZS_ERR_DTYPE;
+  if (!grads) return ZS_ERR_NULL;
+  int64_t m, s, e;
+  shard_bounds(n, p, k, &m, &s, &e);
+  const int64_t len = e - s;
+  if (grad_base < 0 || grad_base > s) return ZS_ERR_RANGE;
+  if (len == 0) return ZS_OK;
+  if (!g_out) return ZS_ERR_NULL;
+  for (int32_t r = 0; r < p; ++r)
+    if (!grads[r]) return ZS_ERR_NULL;
+
+  zs::MeanLaunch L;
+  L.p = p;
+  L.gdt = grad_dtype;
+  L.out = g_out;
+  L.len = len;
+  L.PF = static_cast<float>(static_cast<double>(p));
+  L.stream = static_cast<hipStream_t>(stream);
+  const uintptr_t po = reinterpret_cast<uintptr_t>(g_out);
+  const Range wr{po, po + 4u * static_cast<uintptr_t>(len)};
+  std::vector<uintptr_t> a16;
+  for (int32_t r = 0; r < p; ++r) {
+    L.grads[r] = static_cast<const uint16_t*>(grads[r]) + (s - grad_base);
+    const uintptr_t g0 = reinterpret_cast<uintptr_t>(L.grads[r]);
+    if (overlap(wr, Range{g0, g0 + 2u * static_cast<uintptr_t>(len)})) return ZS_ERR_ALIAS;
+    a16.push_back(g0);
+  }
+  // the fp32 output is written once per element: weigh it like a 16-bit read x2
+  L.head = choose_head(a16, {po});
+  const hipError_t err = zs::launch_mean(L);
+  if (err != hipSuccess) return hip_fail(err);
+  return ZS_OK;
+}
+
+zs_status zs_adam_step(const float* g, float* w, float* m, float* v, void* param,
+                       int32_t param_dtype, int64_t len, const zs_adam_hparams* hp,
+                       void* stream) {
+  if (len < 0) return ZS_ERR_ARG;
+  if (len > kMaxN) return ZS_ERR_RANGE;
+  if (param && !dtype_ok(param_dtype)) return ZS_ERR_DTYPE;
+  if (const zs_status st = check_hparams(hp)) return st;
+  if (len == 0) return ZS_OK;
+  if (!g || !w || !m || !v) return ZS_ERR_NULL;
+  const uintptr_t b32 = 4u * static_cast<uintptr_t>(len), b16 = 2u * static_cast<uintptr_t>(len);
+  const uintptr_t pg = reinterpret_cast<uintptr_t>(g), pw = reinterpret_cast<uintptr_t>(w),
+                  pm = reinterpret_cast<uintptr_t>(m), pv = reinterpret_cast<uintptr_t>(v),
+                  pp = reinterpret_cast<uintptr_t>(param);
+  std::vector<Range> writes = {{pw, pw + b32}, {pm, pm + b32}, {pv, pv + b32}};
+  if (param) writes.push_back({pp, pp + b16});
+  const Range rd{pg, pg + b32};
+  for (size_t i = 0; i < writes.size(); ++i) {
+    if (overlap(writes[i], rd)) return ZS_ERR_ALIAS;
+    for (size_t j = i + 1; j < writes.size(); ++j)
+      if (overlap(writes[i], writes[j])) return ZS_ERR_ALIAS;
+  }
+  zs::AdamLaunch L;
+  L.g = g;
+  L.w = w;
+  L.m = m;
+  L.v = v;
+  L.param = static_cast<uint16_t*>(param);
+  L.pdt = param ? param_dtype : ZS_F16;
+  L.form = hp->form;
+  L.len = len;
+  L.c = make_consts(*hp, 1);
+  L.stream = static_cast<hipStream_t>(stream);
+  std::vector<uintptr_t> a16;
+  if (param) a16.push_back(pp);
+  L.head = choose_head(a16, {pg, pw, pm, pv});
+  const hipError_t err = zs::launch_adam(L);
+  if (err != hipSuccess) return hip_fail(err);
+  return ZS_OK;
+}
+
+// ---------------------------------------------------------------- multi
+
+zs_status zs_plan_chunks(const int64_t* numel, int32_t ntensors, int32_t p, int32_t k,
+                         int64_t chunk_elems, zs_piece* pieces, int32_t pieces_cap,
+                         int32_t* npieces, int64_t* nchunks_out) {
+  if (!npieces || (ntensors > 0 && !numel) || (pieces_cap > 0 && !pieces)) return ZS_ERR_NULL;
+  if (ntensors < 0 || p < 1 || k < 0 || k >= p || pieces_cap < 0 || chunk_elems < 0)
+    return ZS_ERR_ARG;
+  int64_t n = 0;
+  for (int32_t t = 0; t < ntensors; ++t) {
+    if (numel[t] < 0) return ZS_ERR_ARG;
+    n += numel[t];
+    if (n > kMaxN) return ZS_ERR_RANGE;
+  }
+  int64_t m, s, e;
+  shard_bounds(n, p, k, &m, &s, &e);
+  // Walk the tensors with a running offset; each tensor [off, off + numel)
+  // that meets [s, e) gives one piece.
+  int32_t count = 0;
+  int64_t chunks = 0;
+  int64_t off = 0;
+  for (int32_t t = 0; t < ntensors && off < e; ++t) {
+    const int64_t lo = off > s ? off : s;
+    const int64_t hi = off + numel[t] < e ? off + numel[t] : e;
+    if (lo < hi) {
+      if (count < pieces_cap) {
+        zs_piece& pc = pieces[count];
+        pc.tensor = t;
+        pc.reserved = 0;
+        pc.tensor_off = lo - off;
+        pc.shard_off = lo - s;
+        pc.len = hi - lo;
+      }
+      ++count;
+      if (chunk_elems > 0) chunks += (hi - lo + chunk_elems - 1) / chunk_elems;
+    }
+    off += numel[t];
+  }
+  *npieces = count;
+  if (nchunks_out) *nchunks_out = chunks;
+  return count > pieces_cap ? ZS_ERR_CAPACITY : ZS_OK;
+}
+
+}  // extern "C"
+
+namespace zs {
+MtLayout mt_layout(int32_t npieces, int64_t nchunks, int32_t p) {
+  auto up = [](size_t x) { return (x + 255u) & ~static_cast<size_t>(255u); };
+  MtLayout L;
+  L.pieces_off = 0;
+  L.gptr_off = up(sizeof(MtPiece) * static_cast<size_t>(npieces));
+  L.chunks_off = L.gptr_off + up(sizeof(void*) * static_cast<size_t>(npieces) * p);
+  L.total = L.chunks_off + up(sizeof(MtChunk) * static_cast<size_t>(nchunks));
+  if (L.total == 0) L.total = 256;
+  return L;
+}
+}  // namespace zs
+
+extern "C" {
+
+size_t zs_mt_workspace_bytes(int32_t npieces, int64_t nchunks, int32_t p) {
+  if (npieces < 0 || nchunks < 0 || p < 1 || p > ZS_MAX_P) return 0;
+  return zs::mt_layout(npieces, nchunks, p).total;
+}
+
+zs_status zs_mt_upload(const zs_piece* pieces, const zs_piece_ptrs* ptrs, int32_t npieces,
+                       int32_t p, int32_t grad_dtype, int32_t param_dtype, int64_t chunk_elems,
+                       void* workspace, size_t ws_bytes, void* stream, zs_mt_table* table) {
+  if (!table || !workspace || (npieces > 0 && (!pieces || !ptrs))) return ZS_ERR_NULL;
+  if (p < 1 || p > ZS_MAX_P || npieces < 0 || chunk_elems < zs::kVec ||
+      chunk_elems % zs::kVec != 0)
+    return ZS_ERR_ARG;
+  if (!dtype_ok(grad_dtype) || !dtype_ok(param_dtype)) return ZS_ERR_DTYPE;
+  int64_t nchunks = 0;
+  std::vector<Range> writes, reads;
+  for (int32_t i = 0; i < npieces; ++i) {
+    const int64_t len = pieces[i].len;
+    if (len < 1 || len > kMaxN) return ZS_ERR_ARG;
+    const zs_piece_ptrs& q = ptrs[i];
+    if (!q.w || !q.m || !q.v || !q.param || !q.grads) return ZS_ERR_NULL;
+    for (int32_t r = 0; r < p; ++r) {
+      if (!q.grads[r]) return ZS_ERR_NULL;
+      const uintptr_t g0 = reinterpret_cast<uintptr_t>(q.grads[r]);
+      reads.push_back({g0, g0 + 2u * static_cast<uintptr_t>(len)});
+    }
+    const uintptr_t b32 = 4u * static_cast<uintptr_t>(len), b16 = 2u * static_cast<uintptr_t>(len);
+    const uintptr_t pw = reinterpret_cast<uintptr_t>(q.w), pm = reinterpret_cast<uintptr_t>(q.m),
+                    pv = reinterpret_cast<uintptr_t>(q.v),
+                    pp = reinterpret_cast<uintptr_t>(q.param);
+    writes.push_back({pw, pw + b32});
+    writes.push_back({pm, pm + b32});
+    writes.push_back({pv, pv + b32});
+    writes.push_back({pp, pp + b16});
+    nchunks += (len + chunk_elems - 1) / chunk_elems;
+  }
+  // Outputs must be pairwise disjoint and must not overlap any gradient range:
+  // sort both lists and sweep, O((W + R) log(W + R)).
+  auto by_lo = [](const Range& x, const Range& y) { return x.lo < y.lo; };
+  std::sort(writes.begin(), writes.end(), by_lo);
+  std::sort(reads.begin(), reads.end(), by_lo);
+  for (size_t i = 1; i < writes.size(); ++i)
+    if (writes[i].lo < writes[i - 1].hi) return ZS_ERR_ALIAS;
+  {
+    size_t j = 0;
+    uintptr_t reach = 0;  // max hi over reads with lo < current write's hi
+    for (const Range& wr : writes) {
+      while (j < reads.size() && reads[j].lo < wr.hi) {
+        if (reads[j].hi > reach) reach = reads[j].hi;
+        ++j;
+      }
+      // a read that starts before wr.hi and ends after wr.lo overlaps wr
+      if (reach > wr.lo) return ZS_ERR_ALIAS;
+    }
+  }
+  const zs::MtLayout lay = zs::mt_layout(npieces, nchunks, p);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256u != 0 || ws_bytes < lay.total)
+    return ZS_ERR_CAPACITY;
+
+  std::vector<unsigned char> host(lay.total, 0);
+  auto* hp_pieces = reinterpret_cast<zs::MtPiece*>(host.data() + lay.pieces_off);
+  auto* hp_gptr = reinterpret_cast<const uint16_t**>(host.data() + lay.gptr_off);
+  auto* hp_chunks = reinterpret_cast<zs::MtChunk*>(host.data() + lay.chunks_off);
+  int64_t c = 0;
+  for (int32_t i = 0; i < npieces; ++i) {
+    const zs_piece_ptrs& q = ptrs[i];
+    zs::MtPiece& d = hp_pieces[i];
+    d.w = q.w;
+    d.m = q.m;
+    d.v = q.v;
+    d.param = static_cast<uint16_t*>(q.param);
+    d.len = pieces[i].len;
+    d.reserved = 0;
+    std::vector<uintptr_t> a16;
+    for (int32_t r = 0; r < p; ++r) {
+      hp_gptr[static_cast<int64_t>(i) * p + r] = static_cast<const uint16_t*>(q.grads[r]);
+      a16.push_back(reinterpret_cast<uintptr_t>(q.grads[r]));
+    }
+    a16.push_back(reinterpret_cast<uintptr_t>(q.param));
+    d.head = choose_head(a16, {reinterpret_cast<uintptr_t>(q.w), reinterpret_cast<uintptr_t>(q.m),
+                               reinterpret_cast<uintptr_t>(q.v)});
+    for (int64_t st = 0; st < d.len; st += chunk_elems) {
+      hp_chunks[c].piece = i;
+      hp_chunks[c].reserved = 0;
+      hp_chunks[c].start = st;
+      ++c;
+    }
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err = hipMemcpyAsync(workspace, host.data(), lay.total, hipMemcpyHostToDevice, s);
+  if (err != hipSuccess) return hip_fail(err);
+  err = hipStreamSynchronize(s);
+  if (err != hipSuccess) return hip_fail(err);
+  table->workspace = workspace;
+  table->nchunks = nchunks;
+  table->chunk_elems = chunk_elems;
+  table->npieces = npieces;
+  table->p = p;
+  table->grad_dtype = grad_dtype;
+  table->param_dtype = param_dtype;
+  return ZS_OK;
+}
+
+zs_status zs_fused_shard_step_multi(const zs_mt_table* t, const zs_adam_hparams* hp,
+                                    void* stream) {
+  if (!t) return ZS_ERR_NULL;
+  if (const zs_status st = check_hparams(hp)) return st;
+  if (t->p < 1 || t->p > ZS_MAX_P || t->npieces < 0 || t->nchunks < 0 ||
+      t->chunk_elems < zs::kVec || t->chunk_elems % zs::kVec != 0)
+    return ZS_ERR_ARG;
+  if (!dtype_ok(t->grad_dtype) || !dtype_ok(t->param_dtype)) return ZS_ERR_DTYPE;
+  if (t->nchunks == 0) return ZS_OK;
+  if (!t->workspace) return ZS_ERR_NULL;
+  const zs::MtLayout lay = zs::mt_layout(t->npieces, t->nchunks, t->p);
+  const auto* base = static_cast<const unsigned char*>(t->workspace);
+  zs::MultiLaunch L;
+  L.pieces = reinterpret_cast<const zs::MtPiece*>(base + lay.pieces_off);
+  L.gptrs = reinterpret_cast<const uint16_t* const*>(base + lay.gptr_off);
+  L.chunks = reinterpret_cast<const zs::MtChunk*>(base + lay.chunks_off);
+  L.nchunks = t->nchunks;
+  L.chunk_elems = t->chunk_elems;
+  L.p = t->p;
+  L.gdt = t->grad_dtype;
+  L.pdt = t->param_dtype;
+  L.form = hp->form;
+  L.c = make_consts(*hp, t->p);
+  L.stream = static_cast<hipStream_t>(stream);
+  const hipError_t err = zs::launch_multi(L);
+  if (err != hipSuccess) return hip_fail(err);
+  return ZS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,270 @@
+"""Thin ctypes binding of libzshard (include/zshard.h), same names as the C ABI.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libzshard.so.  There is no CPU fallback; if the library is not
+built, every call raises.  Tensors are used for their device addresses;
+plain integers are accepted as addresses too.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libzshard.so")
+
+ZS_OK, ZS_ERR_NULL, ZS_ERR_ARG, ZS_ERR_DTYPE, ZS_ERR_RANGE, ZS_ERR_ALIAS, ZS_ERR_CAPACITY, \
+    ZS_ERR_HIP = range(8)
+ZS_F16, ZS_BF16 = 1, 2
+ZS_ADAM_STANDARD, ZS_ADAM_PAGE1_LITERAL = 0, 1
+ZS_MAX_P = 256
+
+FORMS = {"standard": ZS_ADAM_STANDARD, "page1_literal": ZS_ADAM_PAGE1_LITERAL}
+DTYPE_NAMES = {"f16": ZS_F16, "bf16": ZS_BF16}
+
+
+class ZsError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        name = lib().zs_status_string(status).decode()
+        extra = f" (hipError {lib().zs_last_hip_error()})" if status == ZS_ERR_HIP else ""
+        super().__init__(f"{where}: {name}{extra}")
+
+
+class zs_adam_hparams(C.Structure):
+    _fields_ = [("lr", C.c_double), ("beta1", C.c_double), ("beta2", C.c_double),
+                ("eps", C.c_double), ("step", C.c_int64), ("form", C.c_int32),
+                ("reserved", C.c_int32)]
+
+
+class zs_shard_args(C.Structure):
+    _fields_ = [("n", C.c_int64), ("p", C.c_int32), ("k", C.c_int32),
+                ("grads", C.POINTER(C.c_void_p)), ("grad_dtype", C.c_int32),
+                ("param_dtype", C.c_int32), ("grad_base", C.c_int64),
+                ("w", C.c_void_p), ("m", C.c_void_p), ("v", C.c_void_p),
+                ("param", C.c_void_p), ("param_base", C.c_int64),
+                ("hp", C.POINTER(zs_adam_hparams)), ("stream", C.c_void_p)]
+
+
+class zs_piece(C.Structure):
+    _fields_ = [("tensor", C.c_int32), ("reserved", C.c_int32), ("tensor_off", C.c_int64),
+                ("shard_off", C.c_int64), ("len", C.c_int64)]
+
+
+class zs_piece_ptrs(C.Structure):
+    _fields_ = [("w", C.c_void_p), ("m", C.c_void_p), ("v", C.c_void_p),
+                ("param", C.c_void_p), ("grads", C.POINTER(C.c_void_p))]
+
+
+class zs_mt_table(C.Structure):
+    _fields_ = [("workspace", C.c_void_p), ("nchunks", C.c_int64), ("chunk_elems", C.c_int64),
+                ("npieces", C.c_int32), ("p", C.c_int32), ("grad_dtype", C.c_int32),
+                ("param_dtype", C.c_int32)]
+
+
+EXPORTS = [
+    "zs_status_string", "zs_version", "zs_last_hip_error", "zs_plan_shards",
+    "zs_fused_shard_step", "zs_reduce_scatter_mean_local", "zs_adam_step", "zs_plan_chunks",
+    "zs_mt_workspace_bytes", "zs_mt_upload", "zs_fused_shard_step_multi",
+]
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                               "(there is no CPU fallback)")
+        L = C.CDLL(LIB_PATH)
+        i32, i64, vp = C.c_int32, C.c_int64, C.c_void_p
+        L.zs_status_string.argtypes = [i32]
+        L.zs_status_string.restype = C.c_char_p
+        L.zs_version.argtypes = []
+        L.zs_version.restype = i32
+        L.zs_last_hip_error.argtypes = []
+        L.zs_last_hip_error.restype = i32
+        L.zs_plan_shards.argtypes = [i64, i32, C.POINTER(i64), C.POINTER(i64), C.POINTER(i64)]
+        L.zs_plan_shards.restype = i32
+        L.zs_fused_shard_step.argtypes = [C.POINTER(zs_shard_args)]
+        L.zs_fused_shard_step.restype = i32
+        L.zs_reduce_scatter_mean_local.argtypes = [C.POINTER(vp), i32, i64, i64, i32, i32, vp, vp]
+        L.zs_reduce_scatter_mean_local.restype = i32
+        L.zs_adam_step.argtypes = [vp, vp, vp, vp, vp, i32, i64, C.POINTER(zs_adam_hparams), vp]
+        L.zs_adam_step.restype = i32
+        L.zs_plan_chunks.argtypes = [C.POINTER(i64), i32, i32, i32, i64, C.POINTER(zs_piece), i32,
+                                     C.POINTER(i32), C.POINTER(i64)]
+        L.zs_plan_chunks.restype = i32
+        L.zs_mt_workspace_bytes.argtypes = [i32, i64, i32]
+        L.zs_mt_workspace_bytes.restype = C.c_size_t
+        L.zs_mt_upload.argtypes = [C.POINTER(zs_piece), C.POINTER(zs_piece_ptrs), i32, i32, i32,
+                                   i32, i64, vp, C.c_size_t, vp, C.POINTER(zs_mt_table)]
+        L.zs_mt_upload.restype = i32
+        L.zs_fused_shard_step_multi.argtypes = [C.POINTER(zs_mt_table),
+                                                C.POINTER(zs_adam_hparams), vp]
+        L.zs_fused_shard_step_multi.restype = i32
+        _lib = L
+    return _lib
+
+
+# ----------------------------------------------------------------- marshalling
+
+def _addr(x) -> int | None:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _dtype_of(x, given) -> int:
+    if given is not None:
+        return DTYPE_NAMES[given] if isinstance(given, str) else int(given)
+    import torch
+
+    if x.dtype == torch.float16:
+        return ZS_F16
+    if x.dtype == torch.bfloat16:
+        return ZS_BF16
+    raise ValueError(f"16-bit tensor expected, got {x.dtype}")
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+
+        if torch.cuda.is_available():
+            return torch.cuda.current_stream().cuda_stream
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ptr_array(xs):
+    arr = (C.c_void_p * len(xs))(*[_addr(x) for x in xs])
+    return C.cast(arr, C.POINTER(C.c_void_p)), arr
+
+
+def _check(st: int, where: str):
+    if st != ZS_OK:
+        raise ZsError(st, where)
+
+
+def hparams(lr, beta1, beta2, eps, step, form="standard") -> zs_adam_hparams:
+    f = FORMS[form] if isinstance(form, str) else int(form)
+    return zs_adam_hparams(float(lr), float(beta1), float(beta2), float(eps), int(step), f, 0)
+
+
+# ----------------------------------------------------------------- entry points
+
+def zs_version() -> int:
+    return lib().zs_version()
+
+
+def zs_status_string(status: int) -> str:
+    return lib().zs_status_string(status).decode()
+
+
+def zs_last_hip_error() -> int:
+    return lib().zs_last_hip_error()
+
+
+def zs_plan_shards(n: int, p: int):
+    """(M, starts, ends) for all p ranks."""
+    m = C.c_int64()
+    s = (C.c_int64 * max(p, 1))()
+    e = (C.c_int64 * max(p, 1))()
+    _check(lib().zs_plan_shards(n, p, C.byref(m), s, e), "zs_plan_shards")
+    return m.value, list(s)[:p], list(e)[:p]
+
+
+def zs_fused_shard_step(n, p, k, grads, w, m, v, param, hp: zs_adam_hparams, *,
+                        grad_base=0, param_base=0, grad_dtype=None, param_dtype=None,
+                        stream=None, check=True) -> int:
+    gptr, keep = _ptr_array(grads)
+    a = zs_shard_args(
+        n=n, p=p, k=k, grads=gptr if grads is not None else None,
+        grad_dtype=_dtype_of(grads[0], grad_dtype) if grads else (grad_dtype or ZS_F16),
+        param_dtype=_dtype_of(param, param_dtype) if param is not None else (param_dtype or 0),
+        grad_base=grad_base, w=_addr(w), m=_addr(m), v=_addr(v), param=_addr(param),
+        param_base=param_base, hp=C.pointer(hp), stream=_stream(stream))
+    st = lib().zs_fused_shard_step(C.byref(a))
+    del keep
+    if check:
+        _check(st, "zs_fused_shard_step")
+    return st
+
+
+def zs_reduce_scatter_mean_local(grads, n, p, k, g_out, *, grad_base=0, grad_dtype=None,
+                                 stream=None, check=True) -> int:
+    gptr, keep = _ptr_array(grads)
+    st = lib().zs_reduce_scatter_mean_local(gptr, _dtype_of(grads[0], grad_dtype), grad_base,
+                                            n, p, k, _addr(g_out), _stream(stream))
+    del keep
+    if check:
+        _check(st, "zs_reduce_scatter_mean_local")
+    return st
+
+
+def zs_adam_step(g, w, m, v, param, length: int, hp: zs_adam_hparams, *, param_dtype=None,
+                 stream=None, check=True) -> int:
+    pdt = _dtype_of(param, param_dtype) if param is not None else 0
+    st = lib().zs_adam_step(_addr(g), _addr(w), _addr(m), _addr(v), _addr(param), pdt, length,
+                            C.byref(hp), _stream(stream))
+    if check:
+        _check(st, "zs_adam_step")
+    return st
+
+
+def zs_plan_chunks(numel, p: int, k: int, chunk_elems: int):
+    """([(tensor, tensor_off, shard_off, len), ...], nchunks)."""
+    nm = (C.c_int64 * max(len(numel), 1))(*numel)
+    npieces = C.c_int32()
+    nchunks = C.c_int64()
+    st = lib().zs_plan_chunks(nm, len(numel), p, k, chunk_elems, None, 0, C.byref(npieces),
+                              C.byref(nchunks))
+    if st not in (ZS_OK, ZS_ERR_CAPACITY):
+        _check(st, "zs_plan_chunks")
+    cap = npieces.value
+    arr = (zs_piece * max(cap, 1))()
+    _check(lib().zs_plan_chunks(nm, len(numel), p, k, chunk_elems, arr, cap, C.byref(npieces),
+                                C.byref(nchunks)), "zs_plan_chunks")
+    return [(x.tensor, x.tensor_off, x.shard_off, x.len) for x in arr[:npieces.value]], \
+        nchunks.value
+
+
+def zs_mt_workspace_bytes(npieces: int, nchunks: int, p: int) -> int:
+    return lib().zs_mt_workspace_bytes(npieces, nchunks, p)
+
+
+def zs_mt_upload(pieces, ptrs, p: int, grad_dtype, param_dtype, chunk_elems: int, workspace,
+                 ws_bytes: int, *, stream=None) -> zs_mt_table:
+    """pieces: [(tensor, tensor_off, shard_off, len)]; ptrs: [dict(w, m, v, param, grads)]
+    with device addresses (or tensors) at each piece's first element."""
+    n = len(pieces)
+    pa = (zs_piece * max(n, 1))(*[zs_piece(t, 0, to, so, ln) for (t, to, so, ln) in pieces])
+    keep = []
+    qa = (zs_piece_ptrs * max(n, 1))()
+    for i, q in enumerate(ptrs):
+        gp, g_keep = _ptr_array(q["grads"])
+        keep.append(g_keep)
+        qa[i] = zs_piece_ptrs(_addr(q["w"]), _addr(q["m"]), _addr(q["v"]), _addr(q["param"]), gp)
+    gdt = DTYPE_NAMES[grad_dtype] if isinstance(grad_dtype, str) else int(grad_dtype)
+    pdt = DTYPE_NAMES[param_dtype] if isinstance(param_dtype, str) else int(param_dtype)
+    table = zs_mt_table()
+    st = lib().zs_mt_upload(pa, qa, n, p, gdt, pdt, chunk_elems, _addr(workspace), ws_bytes,
+                            _stream(stream), C.byref(table))
+    del keep
+    _check(st, "zs_mt_upload")
+    return table
+
+
+def zs_fused_shard_step_multi(table: zs_mt_table, hp: zs_adam_hparams, *, stream=None,
+                              check=True) -> int:
+    st = lib().zs_fused_shard_step_multi(C.byref(table), C.byref(hp), _stream(stream))
+    if check:
+        _check(st, "zs_fused_shard_step_multi")
+    return st

@@ -1,0 +1,227 @@
+"""Throughput of the fused per-shard ZeRO Adam step on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input:
+shard plan, gather of the P rank-local gradient slices, rank-order fp32
+mean, Adam moments with bias correction, fp32 master update and the
+16-bit working-copy write-back.  Default workload: the 7.5B-parameter model
+at P=64, rank 63's shard (M = 117,187,500), fp16 gradients.
+
+Prints ONE JSON line on stdout.  Inputs are resident in HBM before the timed
+region; the timed region is K back-to-back steps between two device
+synchronisations, timed with HIP events on the stream the kernel runs on.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import threading
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "shard elements/s and achieved HBM GB/s (% of MI355X peak), fused shard Adam"
+HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = [os.path.join(ROOT, "adam_zs_shard_amd", "csrc", f)
+                  for f in ("zs_kernels.hip", "zs_capi.cpp", "zs_internal.h")]
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None if
+    there are none for this workload or the kernel sources changed since."""
+    try:
+        with open(COUNTERS_FILE) as fh:
+            data = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    rec = data.get(workload)
+    if not rec or rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def _time_steps(run_step, steps: int, warmup: int, stream):
+    import torch
+
+    for i in range(warmup):
+        run_step(i)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(steps):
+        run_step(warmup + i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    return ev0.elapsed_time(ev1) / steps, wall
+
+
+def cpu_baseline(gdt: str, pdt: str, grads_host, w, m, v, threads: int, form: str):
+    """The oracle, as it stands, on a contiguous sample of the same shard,
+    split over `threads` host threads (elements are independent)."""
+    import numpy as np
+
+    import oracle
+
+    n = w.size
+    bounds = np.linspace(0, n, threads + 1).astype(np.int64)
+    param = np.empty(n, np.uint16)
+
+    def run(a, b):
+        oracle.step_elems(gdt, [g[a:b] for g in grads_host], w[a:b], m[a:b], v[a:b], pdt,
+                          1e-3, 0.9, 0.999, 1e-8, 1, form, param=param[a:b])
+
+    ths = [threading.Thread(target=run, args=(int(bounds[i]), int(bounds[i + 1])))
+           for i in range(threads)]
+    t0 = time.perf_counter()
+    for t in ths:
+        t.start()
+    for t in ths:
+        t.join()
+    return time.perf_counter() - t0
+
+
+def host_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def bench_single(args):
+    """Fused single-tensor step on one shard with P separate gradient slices."""
+    import numpy as np
+    import torch
+
+    from adam_zs_shard_amd import zshard as z
+    from zs_synth import WORKLOADS, seed_for
+    from zs_synth.gen import normal
+
+    wl = WORKLOADS[args.workload]
+    k = wl.shards[-1]
+    M, s, e = z.zs_plan_shards(wl.n, wl.p)
+    L = e[k] - s[k]
+    dev = "cuda"
+    td = {"f16": torch.float16, "bf16": torch.bfloat16}
+    print(f"[bench] {wl.name}: N={wl.n} P={wl.p} k={k} L={L}", file=sys.stderr, flush=True)
+    grads = [normal(L, wl.grad_std, seed_for(20261202, r, 1, 1, k), td[wl.grad_dtype], dev)
+             for r in range(wl.p)]
+    w = normal(L, wl.w_std, seed_for(20261202, -1, 0, 2, k), torch.float32, dev)
+    m = torch.zeros_like(w)
+    v = torch.zeros_like(w)
+    if wl.param_layout == "full":
+        param = torch.empty(wl.n, dtype=td[wl.param_dtype], device=dev)
+        pbase = 0
+    else:
+        param = torch.empty(L, dtype=td[wl.param_dtype], device=dev)
+        pbase = s[k]
+    gbase = s[k] if wl.grad_layout == "slice" else 0
+    assert wl.grad_layout == "slice"
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        z.zs_fused_shard_step(wl.n, wl.p, k, grads, w, m, v, param,
+                              z.hparams(wl.lr, wl.beta1, wl.beta2, wl.eps, i + 1, wl.form),
+                              grad_base=gbase, param_base=pbase, stream=stream.cuda_stream)
+
+    ms, wall = _time_steps(step, args.steps, args.warmup, stream)
+    bytes_per_elem = 2 * wl.p + 26
+    launches_per_step = 1
+    elems = L
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        S = min(L, args.cpu_sample)
+        a0 = (L - S) // 2
+        gh = [g[a0:a0 + S].view(torch.int16).cpu().numpy().view(np.uint16) for g in grads]
+        wh = w[a0:a0 + S].cpu().numpy().copy()
+        mh = m[a0:a0 + S].cpu().numpy().copy()
+        vh = v[a0:a0 + S].cpu().numpy().copy()
+        thr = host_threads()
+        secs = cpu_baseline(wl.grad_dtype, wl.param_dtype, gh, wh, mh, vh, thr, wl.form)
+        cpu = {"value": S / secs, "unit": "elements/s", "cores": thr, "kind": "oracle",
+               "sample": f"{S} contiguous elements from the middle of shard {k} "
+                         f"({wl.p} ranks), one step, {secs:.2f} s wall on {thr} threads"}
+    return dict(wl=wl, k=k, elems=elems, ms=ms, wall=wall, bytes_per_elem=bytes_per_elem,
+                launches=launches_per_step, launch_elems=L, cpu=cpu)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="zero_7p5b_p64")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=1 << 24)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the shard step runs on one device and this "
+              f"build has no multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    from adam_zs_shard_amd import zshard as z
+
+    z.lib()  # fails loudly if the HIP library is not built
+
+    r = bench_single(args)
+    wl = r["wl"]
+    ms = r["ms"]
+    elems_per_s = r["elems"] / (ms / 1e3)
+    launch_ms = ms / r["launches"]
+    alg_bytes = r["bytes_per_elem"] * r["launch_elems"]
+    gbs = alg_bytes / (launch_ms / 1e3) / 1e9
+    traffic = measured_traffic(wl.name)
+    out = {
+        "metric": METRIC,
+        "value": elems_per_s,
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "n_params": wl.n, "ranks": wl.p, "shard": r["k"],
+                   "shard_elems": r["elems"], "grad_dtype": wl.grad_dtype,
+                   "param_dtype": wl.param_dtype, "adam_form": wl.form},
+        "hbm_gbs": gbs,
+        "pct_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": alg_bytes,
+                     "bytes_per_element": r["bytes_per_elem"], "kernel_ms": launch_ms},
+        "cpu_baseline": r["cpu"],
+        "wall_s_timed": r["wall"],
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,231 @@
+"""Host-side tests of libzshard's C ABI (no GPU needed, no kernel launched).
+
+The library loads and exports every symbol include/zshard.h declares; the
+host planners match the oracle exactly; every argument error is reported
+before anything reaches the device (fake device addresses are safe here
+because the calls return before any launch).
+"""
+
+import re
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from adam_zs_shard_amd import zshard as z
+
+try:
+    import torch
+
+    _HAVE_GPU = torch.cuda.is_available()
+except Exception:  # pragma: no cover
+    _HAVE_GPU = False
+from zs_synth import gpt2_small_tensors, llama3_8b_tensors
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "zshard.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(zs_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared_functions()
+    assert len(names) == 11
+    L = z.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(z.EXPORTS) == names
+    assert z.zs_version() == 1
+    for st in range(8):
+        assert z.zs_status_string(st).startswith("ZS_")
+    assert z.zs_status_string(99) == "ZS_ERR_UNKNOWN"
+
+
+@pytest.mark.parametrize("n,p", [(0, 1), (1, 1), (9, 4), (1_000_003, 4), (124_439_808, 8),
+                                 (7_500_000_000, 64), (8_030_261_248, 8), (100_000_007, 16),
+                                 (5, 256), (2**40 + 3, 256)])
+def test_plan_matches_oracle(n, p):
+    assert z.zs_plan_shards(n, p) == oracle.plan_shards(n, p)
+
+
+def test_plan_brute_force_small():
+    for n in range(0, 40):
+        for p in range(1, 12):
+            assert z.zs_plan_shards(n, p) == oracle.plan_shards(n, p)
+
+
+def test_plan_rejects():
+    for n, p in ((-1, 2), (5, 0), (5, -3)):
+        with pytest.raises(z.ZsError) as ei:
+            z.zs_plan_shards(n, p)
+        assert ei.value.status == z.ZS_ERR_ARG
+    with pytest.raises(z.ZsError) as ei:
+        z.zs_plan_shards(2**61, 4)
+    assert ei.value.status == z.ZS_ERR_RANGE
+
+
+@pytest.mark.parametrize("tensors", ["gpt2", "llama", "random"])
+def test_plan_chunks_matches_oracle_pieces(tensors):
+    if tensors == "gpt2":
+        numel = [n for _, n in gpt2_small_tensors()]
+    elif tensors == "llama":
+        numel = [n for _, n in llama3_8b_tensors()]
+    else:
+        numel = [int(x) for x in np.random.default_rng(0).integers(0, 50, 40)]
+    for p in (1, 3, 8, 16):
+        _, s, e = oracle.plan_shards(sum(numel), p)
+        for k in range(p):
+            got, nchunks = z.zs_plan_chunks(numel, p, k, 4096)
+            want = oracle.shard_pieces(numel, s[k], e[k])
+            assert got == want
+            assert nchunks == sum(-(-ln // 4096) for *_, ln in want)
+
+
+def test_plan_chunks_capacity():
+    import ctypes as C
+
+    numel = (C.c_int64 * 4)(5, 5, 5, 5)
+    arr = (z.zs_piece * 1)()
+    npieces = C.c_int32()
+    st = z.lib().zs_plan_chunks(numel, 4, 1, 0, 8, arr, 1, C.byref(npieces), None)
+    assert st == z.ZS_ERR_CAPACITY and npieces.value == 4
+
+
+HP = z.hparams(1e-3, 0.9, 0.999, 1e-8, 1)
+FAKE = 1 << 40  # a device-looking address; never dereferenced on these paths
+
+# Every call below with FAKE addresses must be rejected before any launch.
+# They run only where no GPU exists, so a mistake here cannot reach a device.
+no_device = pytest.mark.skipif(_HAVE_GPU, reason="fake device addresses: CPU-only test")
+
+
+def _fused(n=1000, p=4, k=1, grads=None, w=FAKE, m=FAKE + (1 << 30), v=FAKE + (2 << 30),
+           param=FAKE + (3 << 30), hp=HP, gdt=z.ZS_F16, pdt=z.ZS_F16, grad_base=0, param_base=0):
+    if grads is None:
+        grads = [FAKE + ((4 + r) << 30) for r in range(p)]
+    return z.zs_fused_shard_step(n, p, k, grads, w, m, v, param, hp, grad_base=grad_base,
+                                 param_base=param_base, grad_dtype=gdt, param_dtype=pdt,
+                                 check=False)
+
+
+@no_device
+def test_fused_argument_errors():
+    assert _fused(p=0) == z.ZS_ERR_ARG
+    assert _fused(p=257, grads=[FAKE] * 257) == z.ZS_ERR_ARG
+    assert _fused(k=4) == z.ZS_ERR_ARG
+    assert _fused(k=-1) == z.ZS_ERR_ARG
+    assert _fused(n=-5) == z.ZS_ERR_ARG
+    assert _fused(gdt=3) == z.ZS_ERR_DTYPE
+    assert _fused(pdt=0) == z.ZS_ERR_DTYPE
+    assert _fused(hp=z.hparams(1e-3, 0.9, 0.999, 1e-8, 0)) == z.ZS_ERR_ARG
+    assert _fused(hp=z.hparams(1e-3, 1.0, 0.999, 1e-8, 1)) == z.ZS_ERR_ARG
+    assert _fused(hp=z.hparams(float("nan"), 0.9, 0.999, 1e-8, 1)) == z.ZS_ERR_ARG
+    assert _fused(hp=z.hparams(1e-3, 0.9, 0.999, float("inf"), 1)) == z.ZS_ERR_ARG
+    assert _fused(hp=z.hparams(1e-3, 0.9, 0.999, 1e-8, 1, form=2)) == z.ZS_ERR_ARG
+    assert _fused(w=None) == z.ZS_ERR_NULL
+    assert _fused(param=None) == z.ZS_ERR_NULL
+    assert _fused(grads=[FAKE, None, FAKE, FAKE]) == z.ZS_ERR_NULL
+    # shard 1 of 1000 over 4 starts at 250: bases beyond it are out of range
+    assert _fused(grad_base=251) == z.ZS_ERR_RANGE
+    assert _fused(param_base=-1) == z.ZS_ERR_RANGE
+    assert _fused(n=2**61) == z.ZS_ERR_RANGE
+
+
+@no_device
+def test_fused_alias_detection():
+    L = 250  # shard 1 of n=1000 over p=4 is [250, 500)
+    assert _fused(m=FAKE + 4 * L - 4) == z.ZS_ERR_ALIAS          # w and m overlap by one
+    g = [FAKE + ((4 + r) << 30) for r in range(4)]
+    # rank 2 reads [g2 + 500, g2 + 1000) bytes; param's slice starts at param + 500
+    assert _fused(grads=g, param=g[2]) == z.ZS_ERR_ALIAS
+    assert _fused(grads=g, param=g[2] + 498) == z.ZS_ERR_ALIAS   # last byte pair shared
+    # w overlaps a gradient slice
+    assert _fused(grads=g, w=g[0] + 2 * 250) == z.ZS_ERR_ALIAS
+
+
+@no_device
+def test_empty_shard_returns_ok_without_device():
+    # n=9, p=4: shard 3 is empty; nothing may be launched or dereferenced
+    assert _fused(n=9, p=4, k=3, w=None, m=None, v=None, param=None) == z.ZS_OK
+    assert _fused(n=0, p=1, k=0) == z.ZS_OK
+
+
+@no_device
+def test_mean_and_adam_argument_errors():
+    g = [FAKE + (r << 30) for r in range(4)]
+    f = z.zs_reduce_scatter_mean_local
+    assert f(g, 1000, 4, 4, FAKE + (8 << 30), grad_dtype="f16", check=False) == z.ZS_ERR_ARG
+    assert f(g, 1000, 4, 1, None, grad_dtype="f16", check=False) == z.ZS_ERR_NULL
+    assert f(g, 1000, 4, 1, FAKE + (8 << 30), grad_dtype=7, check=False) == z.ZS_ERR_DTYPE
+    assert f(g, 1000, 4, 1, g[1] + 500, grad_dtype="f16", check=False) == z.ZS_ERR_ALIAS
+    assert f(g, 1000, 4, 1, FAKE + (8 << 30), grad_base=300, grad_dtype="f16",
+             check=False) == z.ZS_ERR_RANGE
+    a = z.zs_adam_step
+    base = FAKE
+    assert a(base, base + 4096, base + 8192, base + 12288, None, -1, HP,
+             check=False) == z.ZS_ERR_ARG
+    assert a(base, base + 4096, base + 8192, base + 12288, None, 0, HP, check=False) == z.ZS_OK
+    # 1025 floats from base run one float into w's range
+    assert a(base, base + 4096, base + 8192, base + 12288, None, 1025, HP,
+             check=False) == z.ZS_ERR_ALIAS
+    assert a(None, base + 4096, base + 8192, base + 12288, None, 8, HP,
+             check=False) == z.ZS_ERR_NULL
+    assert a(base, base + 4096, base + 8192, base + 12288, base + 16384, 8, HP, param_dtype=9,
+             check=False) == z.ZS_ERR_DTYPE
+
+
+@no_device
+def test_mt_upload_argument_errors():
+    assert z.zs_mt_workspace_bytes(3, 10, 8) > 0
+    assert z.zs_mt_workspace_bytes(3, 10, 0) == 0
+    assert z.zs_mt_workspace_bytes(-1, 10, 4) == 0
+    pieces = [(0, 0, 0, 100), (1, 0, 100, 50)]
+    ptrs = [dict(w=FAKE, m=FAKE + (1 << 30), v=FAKE + (2 << 30), param=FAKE + (3 << 30),
+                 grads=[FAKE + (4 << 30), FAKE + (5 << 30)]),
+            dict(w=FAKE + 400, m=FAKE + (1 << 30) + 400, v=FAKE + (2 << 30) + 400,
+                 param=FAKE + (6 << 30), grads=[FAKE + (4 << 30) + 200, FAKE + (5 << 30) + 200])]
+    ws = FAKE + (10 << 30)
+    nb = z.zs_mt_workspace_bytes(2, 2, 2)
+
+    def up(pieces=pieces, ptrs=ptrs, p=2, gdt="f16", pdt="f16", ce=64, ws=ws, nb=nb):
+        try:
+            z.zs_mt_upload(pieces, ptrs, p, gdt, pdt, ce, ws, nb)
+        except z.ZsError as e:
+            return e.status
+        return z.ZS_OK
+
+    assert up(ce=12) == z.ZS_ERR_ARG          # not a multiple of 8
+    assert up(ce=0) == z.ZS_ERR_ARG
+    assert up(p=0) == z.ZS_ERR_ARG
+    assert up(pdt=5) == z.ZS_ERR_DTYPE
+    assert up(nb=nb - 1) == z.ZS_ERR_CAPACITY
+    assert up(ws=ws + 8) == z.ZS_ERR_CAPACITY
+    bad = [dict(ptrs[0]), dict(ptrs[1])]
+    bad[1]["w"] = FAKE + 396                     # overlaps piece 0's w by one float
+    assert up(ptrs=bad) == z.ZS_ERR_ALIAS
+    bad = [dict(ptrs[0]), dict(ptrs[1])]
+    bad[1]["param"] = FAKE + (4 << 30) + 100     # param on top of a gradient
+    assert up(ptrs=bad) == z.ZS_ERR_ALIAS
+    bad = [dict(ptrs[0]), dict(ptrs[1])]
+    bad[0]["v"] = None
+    assert up(ptrs=bad) == z.ZS_ERR_NULL
+
+
+@no_device
+def test_multi_step_argument_errors():
+    t = z.zs_mt_table(workspace=FAKE, nchunks=0, chunk_elems=64, npieces=0, p=2, grad_dtype=1,
+                      param_dtype=1)
+    assert z.zs_fused_shard_step_multi(t, HP, check=False) == z.ZS_OK     # nothing to do
+    t.nchunks = 3
+    t.p = 0
+    assert z.zs_fused_shard_step_multi(t, HP, check=False) == z.ZS_ERR_ARG
+    t.p = 2
+    t.grad_dtype = 9
+    assert z.zs_fused_shard_step_multi(t, HP, check=False) == z.ZS_ERR_DTYPE
+    t.grad_dtype = 1
+    assert z.zs_fused_shard_step_multi(t, z.hparams(1e-3, 0.9, 0.999, 1e-8, 0),
+                                       check=False) == z.ZS_ERR_ARG

@@ -1,0 +1,154 @@
+"""GPU parity of the multi-tensor chunk-table step (zs_plan_chunks +
+zs_mt_upload + zs_fused_shard_step_multi) against the oracle, whose map from
+shard index to (tensor, offset) comes from prefix sums over the tensor list,
+not from the chunk table."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from adam_zs_shard_amd import zshard as z
+from zs_synth import seed_for, gpt2_small_tensors, WORKLOADS
+from zs_synth.gen import normal
+from zs_synth import make
+from gpu_util import (DEV, LR, B1, B2, EPS, need_gpu, say, u16, f32, check_f32, check_param,
+                      oracle_step_threaded)
+
+pytestmark = pytest.mark.gpu
+TD = {"f16": torch.float16, "bf16": torch.bfloat16}
+SENTINEL = 0x4B4B
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+    yield
+    torch.cuda.synchronize()
+
+
+class MtCase:
+    """Device buffers of one rank's shard over a flattened tensor list:
+    rank slices of the shard (gradients), flat shard-local w/m/v, and one
+    16-bit working-copy tensor per parameter tensor the shard touches."""
+
+    def __init__(self, numel, p, k, gdt, pdt, chunk, seed):
+        self.numel, self.p, self.k, self.gdt, self.pdt = numel, p, k, gdt, pdt
+        n = sum(numel)
+        self.n = n
+        M, s, e = oracle.plan_shards(n, p)
+        self.s, self.e = s[k], e[k]
+        self.L = L = e[k] - s[k]
+        self.pieces, self.nchunks = z.zs_plan_chunks(numel, p, k, chunk)
+        assert self.pieces == oracle.shard_pieces(numel, s[k], e[k])
+        self.w0 = normal(L, 0.02, seed_for(seed, 1))
+        self.w = self.w0.to(DEV)
+        self.m = torch.zeros_like(self.w)
+        self.v = torch.zeros_like(self.w)
+        self.params = {}
+        for (t, to, so, ln) in self.pieces:
+            if t not in self.params:
+                buf = torch.empty(numel[t], dtype=TD[pdt], device=DEV)
+                buf.view(torch.int16).fill_(SENTINEL)
+                self.params[t] = buf
+        self.grads = [torch.empty(max(L, 1), dtype=TD[gdt], device=DEV) for _ in range(p)]
+        ptrs = []
+        esz = 2
+        for (t, to, so, ln) in self.pieces:
+            ptrs.append(dict(w=self.w.data_ptr() + 4 * so, m=self.m.data_ptr() + 4 * so,
+                             v=self.v.data_ptr() + 4 * so,
+                             param=self.params[t].data_ptr() + esz * to,
+                             grads=[g.data_ptr() + esz * so for g in self.grads]))
+        nb = z.zs_mt_workspace_bytes(len(self.pieces), self.nchunks, p)
+        self.ws = torch.empty(nb, dtype=torch.uint8, device=DEV)
+        self.table = z.zs_mt_upload(self.pieces, ptrs, p, gdt, pdt, chunk, self.ws, nb)
+        assert self.table.nchunks == self.nchunks
+
+    def set_grads(self, step, seed):
+        self.gbits = []
+        for r in range(self.p):
+            g = normal(self.L, 1e-3, seed_for(seed, 2, r, step), TD[self.gdt])
+            self.grads[r][:self.L].copy_(g.to(DEV))
+            self.gbits.append(g.view(torch.int16).numpy().view(np.uint16))
+
+    def step(self, t, form="standard"):
+        z.zs_fused_shard_step_multi(self.table, z.hparams(LR, B1, B2, EPS, t, form))
+
+
+def _scatter(case, flat_bits):
+    """Per-tensor expected working copies from a shard-flat result, using the
+    oracle's prefix-sum map (pieces)."""
+    out = {t: np.full(case.numel[t], SENTINEL, np.uint16) for t in case.params}
+    for (t, to, so, ln) in oracle.shard_pieces(case.numel, case.s, case.e):
+        out[t][to:to + ln] = flat_bits[so:so + ln]
+    return out
+
+
+def _run_and_check(case, steps, seed, form="standard", check_every=True):
+    wh = case.w0.numpy().copy()
+    mh = np.zeros_like(wh)
+    vh = np.zeros_like(wh)
+    for t in range(1, steps + 1):
+        case.set_grads(t, seed)
+        case.step(t, form)
+        ph = oracle_step_threaded(case.gdt, case.gbits, wh, mh, vh, case.pdt, t, form)
+        if check_every or t == steps:
+            torch.cuda.synchronize()
+            tol = 1e-6 if t == 1 else 2e-6
+            d = check_f32(f32(case.w), wh, tol, f"w t={t}")
+            d += check_f32(f32(case.m), mh, tol, f"m t={t}")
+            d += check_f32(f32(case.v), vh, tol, f"v t={t}")
+            exp = _scatter(case, ph)
+            for tt, buf in case.params.items():
+                d += check_param(u16(buf), exp[tt], case.pdt, f"param tensor {tt} t={t}")
+            assert d == 0, f"{d} elements differ in bits at t={t}"
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_tensor_lists_all_shards(seed):
+    rng = np.random.default_rng(seed)
+    numel = [int(x) for x in rng.integers(0, 3000, 40)]
+    numel[5] = 0
+    numel[7] = 1
+    numel += [50_001, 7, 123_457]
+    p = [2, 3, 5, 8][seed]
+    for k in range(p):
+        case = MtCase(numel, p, k, ["f16", "bf16"][seed % 2], ["f16", "bf16"][seed % 2],
+                      [64, 1024, 4096, 65536][seed], seed_for(40, seed, k))
+        _run_and_check(case, 2, seed_for(41, seed, k))
+
+
+def test_gpt2_small_shapes_shard0_ten_steps():
+    wl = WORKLOADS["gpt2_small_p8"]
+    numel = [n for _, n in wl.tensors]
+    case = MtCase(numel, wl.p, 0, wl.grad_dtype, wl.param_dtype, 65536, 42)
+    assert len(case.pieces) == 1
+    say("gpt2 shard 0: 10 steps")
+    _run_and_check(case, wl.steps, 43, check_every=False)
+
+
+@pytest.mark.parametrize("k", [2, 7])
+def test_gpt2_small_shapes_many_pieces(k):
+    wl = WORKLOADS["gpt2_small_p8"]
+    numel = [n for _, n in wl.tensors]
+    case = MtCase(numel, wl.p, k, wl.grad_dtype, wl.param_dtype, 65536, 44 + k)
+    assert len(case.pieces) in (15, 35)
+    say(f"gpt2 shard {k}: {len(case.pieces)} pieces, 2 steps")
+    _run_and_check(case, 2, 46 + k)
+
+
+def test_multi_equals_single_tensor_step():
+    # one tensor, one piece: the table path and the single-shard path agree bit for bit
+    n, p, k = 500_009, 4, 2
+    case = MtCase([n], p, k, "bf16", "bf16", 8192, 47)
+    case.set_grads(1, 48)
+    case.step(1)
+    w = case.w0.to(DEV)
+    m, v = torch.zeros_like(w), torch.zeros_like(w)
+    par = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    par.view(torch.int16).fill_(SENTINEL)
+    z.zs_fused_shard_step(n, p, k, case.grads, w, m, v, par, z.hparams(LR, B1, B2, EPS, 1),
+                          grad_base=case.s)
+    torch.cuda.synchronize()
+    assert torch.equal(w.view(torch.int32), case.w.view(torch.int32))
+    assert torch.equal(par.view(torch.int16), case.params[0].view(torch.int16))

@@ -1,0 +1,96 @@
+"""GPU parity of the unfused pair: zs_reduce_scatter_mean_local (fp32 mean,
+bit-exact) and zs_adam_step, and their composition against the fused step."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from adam_zs_shard_amd import zshard as z
+from zs_synth import seed_for
+from zs_synth.gen import normal
+from zs_synth import make
+from gpu_util import DEV, LR, B1, B2, EPS, need_gpu, u16, f32, to_dev_u16, check_f32, check_param
+
+pytestmark = pytest.mark.gpu
+TD = {"f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+    yield
+    torch.cuda.synchronize()
+
+
+def _bits(n, dt, std, seed):
+    return normal(n, std, seed, TD[dt]).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("p", [1, 4, 13, 64, 256])
+@pytest.mark.parametrize("layout", ["full", "slice"])
+def test_mean_bit_exact(dt, p, layout):
+    n = 40_000 + 37 * p
+    M, s, e = oracle.plan_shards(n, p)
+    k = (p - 1) // 2
+    L = e[k] - s[k]
+    if layout == "full":
+        gb = [_bits(n, dt, 1e-2, seed_for(30, p, r)) for r in range(p)]
+        base = 0
+        host = [b[s[k]:e[k]] for b in gb]
+    else:
+        gb = [_bits(L, dt, 1e-2, seed_for(31, p, r)) for r in range(p)]
+        base = s[k]
+        host = gb
+    gd = [to_dev_u16(b, TD[dt]) for b in gb]
+    out = torch.full((L,), float("nan"), device=DEV)
+    z.zs_reduce_scatter_mean_local(gd, n, p, k, out, grad_base=base)
+    torch.cuda.synchronize()
+    want = oracle.grad_mean(dt, host)
+    assert np.array_equal(f32(out).view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("pdt", ["f16", "bf16", None])
+@pytest.mark.parametrize("form", ["standard", "page1_literal"])
+def test_adam_step_matches_oracle(pdt, form):
+    L = 123_457
+    g = normal(L, 1e-2, seed_for(32)).numpy()
+    w0 = normal(L, 0.02, seed_for(33)).numpy()
+    m0, v0 = (x.numpy() for x in make.random_state(L, 34))
+    gd, wd, md, vd = (torch.from_numpy(x.copy()).to(DEV) for x in (g, w0, m0, v0))
+    par = torch.empty(L, dtype=TD[pdt], device=DEV) if pdt else None
+    for t in (1, 2, 3):
+        z.zs_adam_step(gd, wd, md, vd, par, L, z.hparams(LR, B1, B2, EPS, t, form))
+    torch.cuda.synchronize()
+    wh, mh, vh = w0.copy(), m0.copy(), v0.copy()
+    for t in (1, 2, 3):
+        ph = oracle.adam_apply(g, wh, mh, vh, pdt or "f16", LR, B1, B2, EPS, t, form)
+    assert check_f32(f32(wd), wh, 2e-6, "w") == 0
+    assert check_f32(f32(md), mh, 2e-6, "m") == 0
+    assert check_f32(f32(vd), vh, 2e-6, "v") == 0
+    if pdt:
+        assert check_param(u16(par), ph, pdt, "param") == 0
+
+
+@pytest.mark.parametrize("gdt", ["f16", "bf16"])
+def test_unfused_pair_equals_fused(gdt):
+    n, p, k = 300_007, 6, 4
+    M, s, e = oracle.plan_shards(n, p)
+    L = e[k] - s[k]
+    gd = [normal(n, 1e-3, seed_for(35, r), TD[gdt], "cpu").to(DEV) for r in range(p)]
+    w0 = normal(L, 0.02, seed_for(36)).to(DEV)
+    a = [w0.clone(), torch.zeros_like(w0), torch.zeros_like(w0)]
+    b = [w0.clone(), torch.zeros_like(w0), torch.zeros_like(w0)]
+    pa = torch.zeros(n, dtype=TD[gdt], device=DEV)
+    pb = torch.zeros(L, dtype=TD[gdt], device=DEV)
+    g = torch.empty(L, device=DEV)
+    for t in (1, 2):
+        h = z.hparams(LR, B1, B2, EPS, t)
+        z.zs_fused_shard_step(n, p, k, gd, *a, pa, h)
+        z.zs_reduce_scatter_mean_local(gd, n, p, k, g)
+        z.zs_adam_step(g, *b, pb, L, h)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int32), y.view(torch.int32))
+    assert torch.equal(pa[s[k]:e[k]].view(torch.int16), pb.view(torch.int16))
