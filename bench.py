@@ -164,6 +164,25 @@ def bench_single(args):
                 launches=launches_per_step, launch_elems=L, cpu=cpu)
 
 
+def copy_probe(nbytes: int = 1 << 31, reps: int = 10):
+    """A plain device copy of known size (torch's copy kernel), used to
+    calibrate rocprofv3's FETCH_SIZE / WRITE_SIZE counters: each dispatch
+    reads and writes exactly `nbytes`."""
+    import torch
+
+    src = torch.ones(nbytes // 4, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    print(json.dumps({"copy_probe_bytes_read": nbytes, "copy_probe_bytes_written": nbytes,
+                      "dispatches": reps, "seconds_per_copy": dt,
+                      "gbs_read_plus_write": 2 * nbytes / dt / 1e9}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -172,6 +191,8 @@ def main():
     ap.add_argument("--workload", default="zero_7p5b_p64")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1 << 24)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run only a plain 2 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the shard step runs on one device and this "
@@ -183,6 +204,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_probe:
+        copy_probe()
+        return
     from adam_zs_shard_amd import zshard as z
 
     z.lib()  # fails loudly if the HIP library is not built
