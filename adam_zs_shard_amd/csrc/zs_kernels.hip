@@ -13,7 +13,7 @@
 //    from sinking each load next to its use), then adds them into the
 //    per-group sums.  Every element receives the ranks in order 0..P-1: a
 //    left fold, one fp32 rounding per add, exactly the oracle's order.
-//    Gradient loads are non-temporal.
+//    All loads and stores are non-temporal (each byte is touched once).
 //  - Phase separation: HBM on this part streams reads alone far faster than
 //    reads with any writes mixed in.  A workgroup therefore sums the
 //    gradients of a whole chunk (up to 28 groups per lane, held in registers
@@ -176,13 +176,18 @@ __device__ __forceinline__ u32x4 ld_u16x8(const uint16_t* base, uint32_t off) {
   return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + off);
 }
 __device__ __forceinline__ f32x4 ld_f32x4(const float* base, uint32_t off) {
-  return *reinterpret_cast<const f32x4*>(reinterpret_cast<const char*>(base) + off);
+  return __builtin_nontemporal_load(
+      reinterpret_cast<const f32x4*>(reinterpret_cast<const char*>(base) + off));
 }
+// The fp32 state loads and all stores are non-temporal too: each byte of w,
+// m, v and the working copy is read once and written once per step.  Against
+// plain loads and stores this is about 1.4% faster on the 7.5B-parameter,
+// 64-rank shard; plain gradient loads instead of non-temporal ones cost 10%.
 __device__ __forceinline__ void st_f32x4(float* base, uint32_t off, f32x4 x) {
-  *reinterpret_cast<f32x4*>(reinterpret_cast<char*>(base) + off) = x;
+  __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(reinterpret_cast<char*>(base) + off));
 }
 __device__ __forceinline__ void st_u16x8(uint16_t* base, uint32_t off, u32x4 x) {
-  *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(base) + off) = x;
+  __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(reinterpret_cast<char*>(base) + off));
 }
 
 template <int GDT>
