@@ -190,7 +190,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="zero_7p5b_p64")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=1 << 24)
+    ap.add_argument("--cpu-sample", type=int, default=1 << 25)
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain 2 GiB device copy (counter calibration)")
     args = ap.parse_args()
