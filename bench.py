@@ -6,6 +6,11 @@ mean, Adam moments with bias correction, fp32 master update and the
 16-bit working-copy write-back.  Default workload: the 7.5B-parameter model
 at P=64, rank 63's shard (M = 117,187,500), fp16 gradients.
 
+Other workloads (--workload): the two parameter-list shapes go through the
+multi-tensor chunk table (zs_fused_shard_step_multi, one launch per step);
+the all-shard workloads (full-N gradient buffers) run one zs_fused_shard_step
+launch per shard, P launches per step.
+
 Prints ONE JSON line on stdout.  Inputs are resident in HBM before the timed
 region; the timed region is K back-to-back steps between two device
 synchronisations, timed with HIP events on the stream the kernel runs on.
@@ -164,6 +169,121 @@ def bench_single(args):
                 launches=launches_per_step, launch_elems=L, cpu=cpu)
 
 
+def _cpu_leg(args, wl, grads, w, m, v, label):
+    """The oracle on a contiguous sample of one shard's elements."""
+    import numpy as np
+    import torch
+
+    L = w.numel()
+    S = min(L, args.cpu_sample)
+    a0 = (L - S) // 2
+    gh = [g[a0:a0 + S].view(torch.int16).cpu().numpy().view(np.uint16) for g in grads]
+    wh = w[a0:a0 + S].cpu().numpy().copy()
+    mh = m[a0:a0 + S].cpu().numpy().copy()
+    vh = v[a0:a0 + S].cpu().numpy().copy()
+    thr = host_threads()
+    secs = cpu_baseline(wl.grad_dtype, wl.param_dtype, gh, wh, mh, vh, thr, wl.form)
+    return {"value": S / secs, "unit": "elements/s", "cores": thr, "kind": "oracle",
+            "sample": f"{S} contiguous elements from the middle of {label} ({wl.p} ranks), one "
+                      f"step, {secs:.2f} s wall on {thr} threads"}
+
+
+def bench_multi(args):
+    """Multi-tensor step of one shard of a parameter list, through the chunk table."""
+    import torch
+
+    from adam_zs_shard_amd import zshard as z
+    from zs_synth import WORKLOADS, make
+
+    wl = WORKLOADS[args.workload]
+    k = wl.shards[0]
+    numel = [n for _, n in wl.tensors]
+    M, s, e = z.zs_plan_shards(wl.n, wl.p)
+    L = e[k] - s[k]
+    dev = "cuda"
+    td = {"f16": torch.float16, "bf16": torch.bfloat16}
+    if args.chunk <= 0:
+        whole = 28 * 256 * 8
+        ncu = torch.cuda.get_device_properties(0).multi_processor_count
+        per_cu = -(-L // ncu)
+        args.chunk = whole if L >= 2 * whole * ncu else -(-per_cu // 2048) * 2048
+    pieces, nchunks = z.zs_plan_chunks(numel, wl.p, k, args.chunk)
+    print(f"[bench] {wl.name}: N={wl.n} P={wl.p} k={k} L={L} pieces={len(pieces)} "
+          f"chunks={nchunks} chunk_elems={args.chunk}", file=sys.stderr, flush=True)
+    grads = [make.normal_grad(wl, r, 1, L, dev, stream=k) for r in range(wl.p)]
+    w = make.initial_w(wl, k, L, dev)
+    m = torch.zeros_like(w)
+    v = torch.zeros_like(w)
+    params = {}
+    for (t, _, _, _) in pieces:
+        if t not in params:
+            params[t] = torch.empty(numel[t], dtype=td[wl.param_dtype], device=dev)
+    ptrs = [dict(w=w.data_ptr() + 4 * so, m=m.data_ptr() + 4 * so, v=v.data_ptr() + 4 * so,
+                 param=params[t].data_ptr() + 2 * to, grads=[g.data_ptr() + 2 * so for g in grads])
+            for (t, to, so, ln) in pieces]
+    nb = z.zs_mt_workspace_bytes(len(pieces), nchunks, wl.p)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    table = z.zs_mt_upload(pieces, ptrs, wl.p, wl.grad_dtype, wl.param_dtype, args.chunk, ws, nb,
+                           stream=stream.cuda_stream)
+    torch.cuda.synchronize()
+
+    def step(i):
+        z.zs_fused_shard_step_multi(table, z.hparams(wl.lr, wl.beta1, wl.beta2, wl.eps, i + 1,
+                                                     wl.form), stream=stream.cuda_stream)
+
+    ms, wall = _time_steps(step, args.steps, args.warmup, stream)
+    cpu = None if args.no_cpu_baseline else _cpu_leg(args, wl, grads, w, m, v, f"shard {k}")
+    return dict(wl=wl, k=k, elems=L, ms=ms, wall=wall, bytes_per_elem=2 * wl.p + 26, launches=1,
+                launch_elems=L, cpu=cpu, extra={"pieces": len(pieces), "chunks": nchunks,
+                                                "chunk_elems": args.chunk})
+
+
+def bench_all_shards(args):
+    """One step of every shard of a model with full-N gradient buffers: P launches."""
+    import torch
+
+    from adam_zs_shard_amd import zshard as z
+    from zs_synth import WORKLOADS, make
+
+    wl = WORKLOADS[args.workload]
+    M, s, e = z.zs_plan_shards(wl.n, wl.p)
+    dev = "cuda"
+    td = {"f16": torch.float16, "bf16": torch.bfloat16}
+    print(f"[bench] {wl.name}: N={wl.n} P={wl.p}, all {wl.p} shards per step",
+          file=sys.stderr, flush=True)
+    if wl.grad_kind == "edge":
+        zero = make.edge_zero_mask(wl, wl.n, dev)
+        grads = [make.edge_grad(wl, r, 1, wl.n, zero, s, e, dev) for r in range(wl.p)]
+        del zero
+    else:
+        grads = [make.normal_grad(wl, r, 1, wl.n, dev) for r in range(wl.p)]
+    states = []
+    for k in range(wl.p):
+        w = make.initial_w(wl, k, e[k] - s[k], dev)
+        states.append((w, torch.zeros_like(w), torch.zeros_like(w)))
+    param = torch.empty(wl.n, dtype=td[wl.param_dtype], device=dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    def step(i):
+        hp = z.hparams(wl.lr, wl.beta1, wl.beta2, wl.eps, i + 1, wl.form)
+        for k in range(wl.p):
+            w, m, v = states[k]
+            z.zs_fused_shard_step(wl.n, wl.p, k, grads, w, m, v, param, hp,
+                                  stream=stream.cuda_stream)
+
+    ms, wall = _time_steps(step, args.steps, args.warmup, stream)
+    k0 = wl.p - 1
+    cpu = None
+    if not args.no_cpu_baseline:
+        w, m, v = states[k0]
+        cpu = _cpu_leg(args, wl, [g[s[k0]:e[k0]] for g in grads], w, m, v, f"shard {k0}")
+    return dict(wl=wl, k=None, elems=wl.n, ms=ms, wall=wall, bytes_per_elem=2 * wl.p + 26,
+                launches=wl.p, launch_elems=wl.n / wl.p, cpu=cpu,
+                extra={"launches_per_step": wl.p})
+
+
 def copy_probe(nbytes: int = 1 << 31, reps: int = 10):
     """A plain device copy of known size (torch's copy kernel), used to
     calibrate rocprofv3's FETCH_SIZE / WRITE_SIZE counters: each dispatch
@@ -191,6 +311,10 @@ def main():
     ap.add_argument("--workload", default="zero_7p5b_p64")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1 << 25)
+    ap.add_argument("--chunk", type=int, default=0,
+                    help="chunk-table chunk length in elements (multi-tensor workloads); 0 picks "
+                         "one whole kernel chunk (57,344), or for shards under two of those per "
+                         "CU, the shard split evenly over the CUs (rounded up to 2,048)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain 2 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -211,7 +335,18 @@ def main():
 
     z.lib()  # fails loudly if the HIP library is not built
 
-    r = bench_single(args)
+    from zs_synth import WORKLOADS
+
+    if args.workload not in WORKLOADS:
+        print(f"unknown workload {args.workload}; one of {sorted(WORKLOADS)}", file=sys.stderr)
+        sys.exit(2)
+    wlx = WORKLOADS[args.workload]
+    if wlx.param_layout == "tensors":
+        r = bench_multi(args)
+    elif wlx.grad_layout == "full":
+        r = bench_all_shards(args)
+    else:
+        r = bench_single(args)
     wl = r["wl"]
     ms = r["ms"]
     elems_per_s = r["elems"] / (ms / 1e3)
@@ -232,9 +367,11 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": wl.name, "n_params": wl.n, "ranks": wl.p, "shard": r["k"],
-                   "shard_elems": r["elems"], "grad_dtype": wl.grad_dtype,
-                   "param_dtype": wl.param_dtype, "adam_form": wl.form},
+        "config": dict({"workload": wl.name, "n_params": wl.n, "ranks": wl.p,
+                        "shard": r["k"] if r["k"] is not None else "all",
+                        "elems_per_step": r["elems"], "grad_dtype": wl.grad_dtype,
+                        "param_dtype": wl.param_dtype, "adam_form": wl.form},
+                       **r.get("extra", {})),
         "hbm_gbs": gbs,
         "pct_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
