@@ -250,6 +250,54 @@ __device__ __forceinline__ void sum_ranks8(const Grads& gr, int p, int64_t e0, u
   if (r0 < p) fold_batch<1, GDT>(gr, r0, e0, lane16, acc);
 }
 
+// Two vectors per lane (element offsets e0 and e1): both vectors' loads of
+// ranks r0 .. r0+B-1 in flight together, then the rank-order adds.
+template <int B, int GDT, class Grads>
+__device__ __forceinline__ void fold_batch2(const Grads& gr, int r0, int64_t e0, int64_t e1,
+                                            uint32_t lane16, float (&a)[kVec], float (&b)[kVec]) {
+  u32x4 qa[B], qb[B];
+#pragma unroll
+  for (int i = 0; i < B; ++i) {
+    qa[i] = ld_grad(gr.get(r0 + i) + e0, lane16);
+    qb[i] = ld_grad(gr.get(r0 + i) + e1, lane16);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (r0 == 0) {
+    init8<GDT>(a, qa[0]);
+    init8<GDT>(b, qb[0]);
+  } else {
+    fold8<GDT>(a, qa[0]);
+    fold8<GDT>(b, qb[0]);
+  }
+#pragma unroll
+  for (int i = 1; i < B; ++i) {
+    fold8<GDT>(a, qa[i]);
+    fold8<GDT>(b, qb[i]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int GDT, class Grads>
+__device__ __forceinline__ void sum_ranks8x2(const Grads& gr, int p, int64_t e0, int64_t e1,
+                                             uint32_t lane16, float (&a)[kVec],
+                                             float (&b)[kVec]) {
+  int r0 = 0;
+  for (; r0 + 16 <= p; r0 += 16) fold_batch2<16, GDT>(gr, r0, e0, e1, lane16, a, b);
+  if (r0 + 8 <= p) {
+    fold_batch2<8, GDT>(gr, r0, e0, e1, lane16, a, b);
+    r0 += 8;
+  }
+  if (r0 + 4 <= p) {
+    fold_batch2<4, GDT>(gr, r0, e0, e1, lane16, a, b);
+    r0 += 4;
+  }
+  if (r0 + 2 <= p) {
+    fold_batch2<2, GDT>(gr, r0, e0, e1, lane16, a, b);
+    r0 += 2;
+  }
+  if (r0 < p) fold_batch2<1, GDT>(gr, r0, e0, e1, lane16, a, b);
+}
+
 // Rank-order mean of one element, kRankBatch loads in flight per batch.
 template <int GDT, class Grads>
 __device__ __forceinline__ float mean1(const Grads& gr, int p, int64_t e, float PF) {
@@ -309,8 +357,51 @@ __device__ __forceinline__ void adam8(const Consts& c, const float (&x)[kVec], f
                    narrow2<PDT>(W[6], W[7])});
 }
 
+// adam8 (DIVIDE form) for two vectors per lane: the state loads of both are
+// issued together, then the arithmetic and stores of each.
+template <int PDT, int FORM>
+__device__ __forceinline__ void adam8x2(const Consts& c, const float (&a)[kVec],
+                                        const float (&b)[kVec], float* w, float* m, float* v,
+                                        uint16_t* par, int64_t e0, int64_t e1, uint32_t lane16,
+                                        uint32_t lane32) {
+  f32x4 S[2][6];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int64_t e = q == 0 ? e0 : e1;
+    S[q][0] = ld_f32x4(w + e, lane32);
+    S[q][1] = ld_f32x4(w + e, lane32 + 16);
+    S[q][2] = ld_f32x4(m + e, lane32);
+    S[q][3] = ld_f32x4(m + e, lane32 + 16);
+    S[q][4] = ld_f32x4(v + e, lane32);
+    S[q][5] = ld_f32x4(v + e, lane32 + 16);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int64_t e = q == 0 ? e0 : e1;
+    const float(&x)[kVec] = q == 0 ? a : b;
+    float W[kVec] = {S[q][0].x, S[q][0].y, S[q][0].z, S[q][0].w,
+                     S[q][1].x, S[q][1].y, S[q][1].z, S[q][1].w};
+    float M[kVec] = {S[q][2].x, S[q][2].y, S[q][2].z, S[q][2].w,
+                     S[q][3].x, S[q][3].y, S[q][3].z, S[q][3].w};
+    float V[kVec] = {S[q][4].x, S[q][4].y, S[q][4].z, S[q][4].w,
+                     S[q][5].x, S[q][5].y, S[q][5].z, S[q][5].w};
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) adam1<FORM>(c, x[j] / c.PF, W[j], M[j], V[j]);
+    st_f32x4(w + e, lane32, f32x4{W[0], W[1], W[2], W[3]});
+    st_f32x4(w + e, lane32 + 16, f32x4{W[4], W[5], W[6], W[7]});
+    st_f32x4(m + e, lane32, f32x4{M[0], M[1], M[2], M[3]});
+    st_f32x4(m + e, lane32 + 16, f32x4{M[4], M[5], M[6], M[7]});
+    st_f32x4(v + e, lane32, f32x4{V[0], V[1], V[2], V[3]});
+    st_f32x4(v + e, lane32 + 16, f32x4{V[4], V[5], V[6], V[7]});
+    st_u16x8(par + e, lane16,
+             u32x4{narrow2<PDT>(W[0], W[1]), narrow2<PDT>(W[2], W[3]), narrow2<PDT>(W[4], W[5]),
+                   narrow2<PDT>(W[6], W[7])});
+  }
+}
+
 // The part of a shard that whole kGroupsMax chunks do not cover: the leftover
-// groups (one vector of 8 elements per lane, kBlock vectors per piece) and the
+// groups (two vectors of 8 elements per lane, 2 * kBlock vectors per piece) and the
 // scalar head and tail elements.  left0 is the first vector after the whole
 // chunks.  Whole chunks go round-robin, so blocks nfull % nblk, ... have one
 // chunk fewer than the rest: the pieces are dealt out starting there, then the
@@ -327,11 +418,17 @@ __device__ __forceinline__ void fused_rest(const Grads& gr, int p, float* __rest
   const int tid = threadIdx.x;
   const int64_t first = nfull % nblk;
   const int64_t me = (blk - first + nblk) % nblk;  // this block's rank in the deal
-  const int64_t npieces = (nvec - left0 + kBlock - 1) / kBlock;
+  constexpr int64_t kPiece = 2 * kBlock;  // vectors per piece: two per lane
+  const int64_t npieces = (nvec - left0 + kPiece - 1) / kPiece;
   for (int64_t i = me; i < npieces; i += nblk) {
-    const int64_t gb = left0 + i * kBlock;
-    if (gb + tid < nvec) {
-      const int64_t e0 = h + gb * kVec;
+    const int64_t gb = left0 + i * kPiece;
+    const int64_t e0 = h + gb * kVec;
+    const int64_t e1 = e0 + static_cast<int64_t>(kBlock) * kVec;
+    if (gb + kBlock + tid < nvec) {
+      float a[kVec], b[kVec];
+      sum_ranks8x2<GDT>(gr, p, e0, e1, lane16, a, b);
+      adam8x2<PDT, FORM>(c, a, b, w, m, v, par, e0, e1, lane16, lane32);
+    } else if (gb + tid < nvec) {
       float g[kVec];
       sum_ranks8<GDT>(gr, p, e0, lane16, g);
       adam8<PDT, FORM, true, true>(c, g, w, m, v, par, e0, lane16, lane32);
