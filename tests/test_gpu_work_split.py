@@ -1,0 +1,82 @@
+"""GPU parity across the single-tensor kernel's work-split regimes, every
+element checked against the oracle.
+
+The kernel runs whole chunks (28 vectors of 8 elements per lane, 57,344
+elements per block) in balanced rounds over its blocks (one per CU), keeps a
+last partial round only when it fills at least half of the blocks, and
+deals the rest out as two-vector pieces.  The shard lengths below are chosen
+from the device's CU count to land in each regime: a last round under half
+full (whole rounds + pieces), one over half full (whole chunks only, plus a
+short tail), a shard smaller than one round (pieces only), and lengths that
+leave every head / scalar-tail combination.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from adam_zs_shard_amd import zshard as z
+from zs_synth import seed_for
+from zs_synth.gen import normal
+from gpu_util import DEV, LR, B1, B2, EPS, need_gpu, say, u16, f32, check_f32, check_param, \
+    oracle_step_threaded
+
+pytestmark = pytest.mark.gpu
+TD = {"f16": torch.float16, "bf16": torch.bfloat16}
+CHUNK = 28 * 256 * 8
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    need_gpu()
+    yield
+    torch.cuda.synchronize()
+
+
+def _cu():
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+def _run(L, p, gdt, steps, seed, offset=0):
+    """Shard k = 0 of n = L * p with slice-layout gradients; the working copy
+    is written at `offset` elements into a larger buffer (alignment)."""
+    n = L * p
+    M, s, e = z.zs_plan_shards(n, p)
+    assert e[0] - s[0] == L
+    w0 = normal(L, 0.02, seed_for(seed, 1))
+    w, m, v = w0.to(DEV), torch.zeros(L, device=DEV), torch.zeros(L, device=DEV)
+    parbuf = torch.zeros(L + 16, dtype=TD[gdt], device=DEV)
+    par = parbuf[offset:offset + L]
+    wh, mh, vh = w0.numpy().copy(), np.zeros(L, np.float32), np.zeros(L, np.float32)
+    for t in range(1, steps + 1):
+        gh = [normal(L, 1e-3, seed_for(seed, 2, r, t), TD[gdt]) for r in range(p)]
+        gd = [g.to(DEV) for g in gh]
+        z.zs_fused_shard_step(n, p, 0, gd, w, m, v, par, z.hparams(LR, B1, B2, EPS, t),
+                              grad_base=0, param_base=0)
+        bits = [g.view(torch.int16).numpy().view(np.uint16) for g in gh]
+        ph = oracle_step_threaded(gdt, bits, wh, mh, vh, gdt, t)
+    torch.cuda.synchronize()
+    d = check_f32(f32(w), wh, 2e-6, "w") + check_f32(f32(m), mh, 2e-6, "m")
+    d += check_f32(f32(v), vh, 2e-6, "v") + check_param(u16(par), ph, gdt, "param")
+    assert d == 0, f"{d} elements differ in bits"
+    canary = u16(parbuf)
+    assert not canary[:offset].any() and not canary[offset + L:].any(), "write outside the shard"
+
+
+@pytest.mark.parametrize("regime", ["rounds_plus_pieces", "all_whole", "pieces_only"])
+def test_work_split_regimes(regime):
+    cu = _cu()
+    rounds_whole = {"rounds_plus_pieces": cu + cu // 4,     # last round a quarter full
+                    "all_whole": cu + (3 * cu) // 4,       # last round three quarters full
+                    "pieces_only": cu // 3}[regime]
+    L = rounds_whole * CHUNK + 8 * 333 + 5
+    say(f"{regime}: {rounds_whole} whole chunks' worth on {cu} CUs, L={L}")
+    _run(L, 2, "f16", 2, seed_for(60, len(regime)))
+
+
+@pytest.mark.parametrize("tail,offset", [(0, 0), (1, 3), (7, 1), (3, 4), (6, 6)])
+def test_work_split_heads_and_tails(tail, offset):
+    cu = _cu()
+    L = (cu // 2) * CHUNK + 8 * 511 + tail
+    _run(L, 3, "bf16", 1, seed_for(61, tail, offset), offset=offset)
