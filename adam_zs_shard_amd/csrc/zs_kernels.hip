@@ -177,9 +177,6 @@ __device__ __forceinline__ u32x4 ld_grad(const uint16_t* base, uint32_t off) {
   return __builtin_nontemporal_load(
       reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + off));
 }
-__device__ __forceinline__ u32x4 ld_u16x8(const uint16_t* base, uint32_t off) {
-  return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + off);
-}
 __device__ __forceinline__ f32x4 ld_f32x4(const float* base, uint32_t off) {
   return __builtin_nontemporal_load(
       reinterpret_cast<const f32x4*>(reinterpret_cast<const char*>(base) + off));

@@ -154,7 +154,11 @@ zs_status zs_adam_step(const float* g, float* w, float* m, float* v, void* param
  * A shard of a flattened parameter list meets several tensors.  Each
  * intersection is a piece; pieces are cut into chunks of at most
  * chunk_elems elements, and one persistent launch walks the chunk table
- * (the analogue of gradient buckets, [ZA] §1.4 ZeRO-R and §1.5). */
+ * (the analogue of gradient buckets, [ZA] §1.4 ZeRO-R and §1.5).  One
+ * workgroup per CU takes one chunk at a time, so the chunk is the unit of
+ * load balance.  A good chunk_elems is 57,344 (= 28 * 256 * 8, the kernel's
+ * whole chunk).  For a shard under two of those per CU, use the shard
+ * length divided by the CU count, rounded up to a multiple of 2,048. */
 typedef struct {
   int32_t tensor;      /* index in the caller's tensor list */
   int32_t reserved;
