@@ -19,9 +19,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liboracle.so")
 
 F16, BF16 = 1, 2
-STANDARD, PAGE1_LITERAL = 0, 1
+STANDARD, PAGE1_LITERAL, SGD, SGD_MOMENTUM = 0, 1, 2, 3
 DTYPES = {"f16": F16, "bf16": BF16}
-FORMS = {"standard": STANDARD, "page1_literal": PAGE1_LITERAL}
+FORMS = {"standard": STANDARD, "page1_literal": PAGE1_LITERAL, "sgd": SGD,
+         "sgd_momentum": SGD_MOMENTUM}
 
 _i64p = C.POINTER(C.c_int64)
 _i32p = C.POINTER(C.c_int32)

@@ -32,7 +32,7 @@ static_assert(sizeof(float) == 4 && sizeof(double) == 8, "IEEE binary32/binary64
 namespace {
 
 enum { DT_F16 = 1, DT_BF16 = 2 };
-enum { FORM_STANDARD = 0, FORM_PAGE1_LITERAL = 1 };
+enum { FORM_STANDARD = 0, FORM_PAGE1_LITERAL = 1, FORM_SGD = 2, FORM_SGD_MOMENTUM = 3 };
 
 uint32_t bits_of(float x) { uint32_t b; std::memcpy(&b, &x, 4); return b; }
 float float_of(uint32_t b) { float x; std::memcpy(&x, &b, 4); return x; }
@@ -183,7 +183,22 @@ float mean_of(int gdt, int32_t p, const uint16_t* const* g, int64_t idx, float P
 //   update  w' = w - lr * mh / (sqrt(vh) + eps)   ([DP-III] §(一) update
 //     equation: eps added outside the square root).
 // Each operation is rounded once, in the order written.
+//
+// The two SGD forms ride on the same call (m, v are left alone when unused):
+//   SGD: w' = w - lr * g   ([DP-III] §(一), the SGD update equation).
+//   SGD_MOMENTUM: m' = beta1*m + g; w' = w - lr * m'.  [ZA] §1.1.1 names
+//     SGD with momentum and its stored momentum buffer but prints no formula;
+//     this is the plain heavy-ball reading, coefficient beta1, m0 = 0.
 void adam_one(const Scalars& c, int form, float g, float* w, float* m, float* v) {
+  if (form == FORM_SGD) {
+    *w = *w - (c.LR * g);
+    return;
+  }
+  if (form == FORM_SGD_MOMENTUM) {
+    *m = (c.B1 * *m) + g;
+    *w = *w - (c.LR * *m);
+    return;
+  }
   const float mm = (c.B1 * *m) + (c.C1 * g);
   const float vv = (c.B2 * *v) + (c.C2 * (g * g));
   float mh, vh;
@@ -205,7 +220,7 @@ void adam_one(const Scalars& c, int form, float g, float* w, float* m, float* v)
 
 bool hparams_ok(double lr, double b1, double b2, double eps, int64_t t, int form) {
   return std::isfinite(lr) && std::isfinite(eps) && b1 >= 0.0 && b1 < 1.0 && b2 >= 0.0 &&
-         b2 < 1.0 && t >= 1 && (form == FORM_STANDARD || form == FORM_PAGE1_LITERAL);
+         b2 < 1.0 && t >= 1 && form >= FORM_STANDARD && form <= FORM_SGD_MOMENTUM;
 }
 
 bool nearest_mode() { return std::fegetround() == FE_TONEAREST; }
