@@ -34,10 +34,15 @@ zs_status check_hparams(const zs_adam_hparams* hp) {
   if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0)) return ZS_ERR_ARG;
   if (!(hp->beta2 >= 0.0 && hp->beta2 < 1.0)) return ZS_ERR_ARG;
   if (hp->step < 1) return ZS_ERR_ARG;
-  if (hp->form != ZS_ADAM_STANDARD && hp->form != ZS_ADAM_PAGE1_LITERAL) return ZS_ERR_ARG;
+  if (hp->form < ZS_ADAM_STANDARD || hp->form > ZS_SGD_MOMENTUM) return ZS_ERR_ARG;
   if (hp->reserved != 0) return ZS_ERR_ARG;
   return ZS_OK;
 }
+
+// Optimizer state a form reads and writes: Adam m and v, momentum SGD m,
+// plain SGD neither.
+bool needs_m(int32_t form) { return form != ZS_SGD; }
+bool needs_v(int32_t form) { return form == ZS_ADAM_STANDARD || form == ZS_ADAM_PAGE1_LITERAL; }
 
 // fp32 constants of one step: each computed in double and rounded once.
 zs::Consts make_consts(const zs_adam_hparams& hp, int32_t p) {
@@ -136,7 +141,8 @@ zs_status zs_fused_shard_step(const zs_shard_args* a) {
   if (a->grad_base < 0 || a->grad_base > s || a->param_base < 0 || a->param_base > s)
     return ZS_ERR_RANGE;
   if (len == 0) return ZS_OK;
-  if (!a->w || !a->m || !a->v || !a->param) return ZS_ERR_NULL;
+  const bool um = needs_m(a->hp->form), uv = needs_v(a->hp->form);
+  if (!a->w || !a->param || (um && !a->m) || (uv && !a->v)) return ZS_ERR_NULL;
   for (int32_t r = 0; r < a->p; ++r)
     if (!a->grads[r]) return ZS_ERR_NULL;
 
@@ -165,15 +171,24 @@ zs_status zs_fused_shard_step(const zs_shard_args* a) {
                   pv = reinterpret_cast<uintptr_t>(L.v),
                   pp = reinterpret_cast<uintptr_t>(L.param);
   const uintptr_t b32 = 4u * static_cast<uintptr_t>(len), b16 = 2u * static_cast<uintptr_t>(len);
-  const Range writes[4] = {{pw, pw + b32}, {pm, pm + b32}, {pv, pv + b32}, {pp, pp + b16}};
-  for (int i = 0; i < 4; ++i) {
-    for (int j = i + 1; j < 4; ++j)
+  // only the buffers the form writes are checked (and used to pick the head)
+  std::vector<Range> writes = {{pw, pw + b32}, {pp, pp + b16}};
+  a32 = {pw};
+  if (um) {
+    writes.push_back({pm, pm + b32});
+    a32.push_back(pm);
+  }
+  if (uv) {
+    writes.push_back({pv, pv + b32});
+    a32.push_back(pv);
+  }
+  for (size_t i = 0; i < writes.size(); ++i) {
+    for (size_t j = i + 1; j < writes.size(); ++j)
       if (overlap(writes[i], writes[j])) return ZS_ERR_ALIAS;
     for (const Range& rd : reads)
       if (overlap(writes[i], rd)) return ZS_ERR_ALIAS;
   }
   a16.push_back(pp);
-  a32 = {pw, pm, pv};
   L.head = choose_head(a16, a32);
 
   const hipError_t err = zs::launch_fused(L);
@@ -228,12 +243,22 @@ zs_status zs_adam_step(const float* g, float* w, float* m, float* v, void* param
   if (param && !dtype_ok(param_dtype)) return ZS_ERR_DTYPE;
   if (const zs_status st = check_hparams(hp)) return st;
   if (len == 0) return ZS_OK;
-  if (!g || !w || !m || !v) return ZS_ERR_NULL;
+  const bool um = needs_m(hp->form), uv = needs_v(hp->form);
+  if (!g || !w || (um && !m) || (uv && !v)) return ZS_ERR_NULL;
   const uintptr_t b32 = 4u * static_cast<uintptr_t>(len), b16 = 2u * static_cast<uintptr_t>(len);
   const uintptr_t pg = reinterpret_cast<uintptr_t>(g), pw = reinterpret_cast<uintptr_t>(w),
                   pm = reinterpret_cast<uintptr_t>(m), pv = reinterpret_cast<uintptr_t>(v),
                   pp = reinterpret_cast<uintptr_t>(param);
-  std::vector<Range> writes = {{pw, pw + b32}, {pm, pm + b32}, {pv, pv + b32}};
+  std::vector<Range> writes = {{pw, pw + b32}};
+  std::vector<uintptr_t> a32 = {pg, pw};
+  if (um) {
+    writes.push_back({pm, pm + b32});
+    a32.push_back(pm);
+  }
+  if (uv) {
+    writes.push_back({pv, pv + b32});
+    a32.push_back(pv);
+  }
   if (param) writes.push_back({pp, pp + b16});
   const Range rd{pg, pg + b32};
   for (size_t i = 0; i < writes.size(); ++i) {
@@ -254,7 +279,7 @@ zs_status zs_adam_step(const float* g, float* w, float* m, float* v, void* param
   L.stream = static_cast<hipStream_t>(stream);
   std::vector<uintptr_t> a16;
   if (param) a16.push_back(pp);
-  L.head = choose_head(a16, {pg, pw, pm, pv});
+  L.head = choose_head(a16, a32);
   const hipError_t err = zs::launch_adam(L);
   if (err != hipSuccess) return hip_fail(err);
   return ZS_OK;
@@ -334,12 +359,15 @@ zs_status zs_mt_upload(const zs_piece* pieces, const zs_piece_ptrs* ptrs, int32_
     return ZS_ERR_ARG;
   if (!dtype_ok(grad_dtype) || !dtype_ok(param_dtype)) return ZS_ERR_DTYPE;
   int64_t nchunks = 0;
+  bool all_m = true, all_v = true;  // every piece has a momentum / variance buffer
   std::vector<Range> writes, reads;
   for (int32_t i = 0; i < npieces; ++i) {
     const int64_t len = pieces[i].len;
     if (len < 1 || len > kMaxN) return ZS_ERR_ARG;
     const zs_piece_ptrs& q = ptrs[i];
-    if (!q.w || !q.m || !q.v || !q.param || !q.grads) return ZS_ERR_NULL;
+    if (!q.w || !q.param || !q.grads) return ZS_ERR_NULL;
+    all_m = all_m && q.m;
+    all_v = all_v && q.v;
     for (int32_t r = 0; r < p; ++r) {
       if (!q.grads[r]) return ZS_ERR_NULL;
       const uintptr_t g0 = reinterpret_cast<uintptr_t>(q.grads[r]);
@@ -350,8 +378,8 @@ zs_status zs_mt_upload(const zs_piece* pieces, const zs_piece_ptrs* ptrs, int32_
                     pv = reinterpret_cast<uintptr_t>(q.v),
                     pp = reinterpret_cast<uintptr_t>(q.param);
     writes.push_back({pw, pw + b32});
-    writes.push_back({pm, pm + b32});
-    writes.push_back({pv, pv + b32});
+    if (q.m) writes.push_back({pm, pm + b32});
+    if (q.v) writes.push_back({pv, pv + b32});
     writes.push_back({pp, pp + b16});
     nchunks += (len + chunk_elems - 1) / chunk_elems;
   }
@@ -398,8 +426,10 @@ zs_status zs_mt_upload(const zs_piece* pieces, const zs_piece_ptrs* ptrs, int32_
       a16.push_back(reinterpret_cast<uintptr_t>(q.grads[r]));
     }
     a16.push_back(reinterpret_cast<uintptr_t>(q.param));
-    d.head = choose_head(a16, {reinterpret_cast<uintptr_t>(q.w), reinterpret_cast<uintptr_t>(q.m),
-                               reinterpret_cast<uintptr_t>(q.v)});
+    std::vector<uintptr_t> a32 = {reinterpret_cast<uintptr_t>(q.w)};
+    if (q.m) a32.push_back(reinterpret_cast<uintptr_t>(q.m));
+    if (q.v) a32.push_back(reinterpret_cast<uintptr_t>(q.v));
+    d.head = choose_head(a16, a32);
     for (int64_t st = 0; st < d.len; st += chunk_elems) {
       hp_chunks[c].piece = i;
       hp_chunks[c].reserved = 0;
@@ -419,6 +449,8 @@ zs_status zs_mt_upload(const zs_piece* pieces, const zs_piece_ptrs* ptrs, int32_
   table->p = p;
   table->grad_dtype = grad_dtype;
   table->param_dtype = param_dtype;
+  table->state = (all_m ? ZS_STATE_M : 0) | (all_v ? ZS_STATE_V : 0);
+  table->reserved = 0;
   return ZS_OK;
 }
 
@@ -431,6 +463,9 @@ zs_status zs_fused_shard_step_multi(const zs_mt_table* t, const zs_adam_hparams*
     return ZS_ERR_ARG;
   if (!dtype_ok(t->grad_dtype) || !dtype_ok(t->param_dtype)) return ZS_ERR_DTYPE;
   if (t->nchunks == 0) return ZS_OK;
+  if ((needs_m(hp->form) && !(t->state & ZS_STATE_M)) ||
+      (needs_v(hp->form) && !(t->state & ZS_STATE_V)))
+    return ZS_ERR_NULL;
   if (!t->workspace) return ZS_ERR_NULL;
   const zs::MtLayout lay = zs::mt_layout(t->npieces, t->nchunks, t->p);
   const auto* base = static_cast<const unsigned char*>(t->workspace);

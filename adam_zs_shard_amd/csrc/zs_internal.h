@@ -8,7 +8,7 @@
 namespace zs {
 
 enum : int { kF16 = 1, kBF16 = 2 };
-enum : int { kStandard = 0, kPage1Literal = 1 };
+enum : int { kStandard = 0, kPage1Literal = 1, kSgd = 2, kSgdMomentum = 3 };
 
 // Elements handled by one lane per vector group: 8 x 16-bit = one 16-byte
 // load per gradient rank; 8 x fp32 = two 16-byte loads per state array.

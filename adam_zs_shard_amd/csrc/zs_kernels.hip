@@ -105,11 +105,20 @@ __device__ __forceinline__ uint32_t narrow2(float lo, float hi) {
   return static_cast<uint32_t>(narrow1<DT>(lo)) | (static_cast<uint32_t>(narrow1<DT>(hi)) << 16);
 }
 
-// One Adam update of one element, in place.  Operation order: the two moment
+// One update of one element, in place.  Adam (both forms): the two moment
 // products rounded, their sum rounded; bias correction by division;
-// d = sqrt(v_hat) + eps; u = m_hat / d; w - lr*u.
+// d = sqrt(v_hat) + eps; u = m_hat / d; w - lr*u.  The SGD forms touch only
+// what they use: w - lr*g, or m = beta1*m + g then w - lr*m.
 template <int FORM>
 __device__ __forceinline__ void adam1(const Consts& c, float g, float& w, float& m, float& v) {
+  if constexpr (FORM == kSgd) {  // w - lr*g; m, v unused
+    w = w - c.LR * g;
+    return;
+  } else if constexpr (FORM == kSgdMomentum) {  // heavy-ball: m = beta1*m + g; w - lr*m
+    m = c.B1 * m + g;
+    w = w - c.LR * m;
+    return;
+  }
   const float mm = c.B1 * m + c.C1 * g;
   const float vv = c.B2 * v + c.C2 * (g * g);
   float mh, vh;
@@ -190,6 +199,38 @@ __device__ __forceinline__ void st_f32x4(float* base, uint32_t off, f32x4 x) {
 }
 __device__ __forceinline__ void st_u16x8(uint16_t* base, uint32_t off, u32x4 x) {
   __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(reinterpret_cast<char*>(base) + off));
+}
+
+// Which optimizer state a form reads and writes: Adam both moments, momentum
+// SGD the momentum only, plain SGD neither (those pointers may be null).
+template <int FORM>
+constexpr bool kUsesM = FORM != kSgd;
+template <int FORM>
+constexpr bool kUsesV = FORM == kStandard || FORM == kPage1Literal;
+
+template <bool USE>
+__device__ __forceinline__ f32x4 ld_state(const float* base, uint32_t off) {
+  if constexpr (USE) {
+    return ld_f32x4(base, off);
+  } else {
+    return f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+}
+template <bool USE>
+__device__ __forceinline__ void st_state(float* base, uint32_t off, f32x4 x) {
+  if constexpr (USE) st_f32x4(base, off, x);
+}
+template <bool USE>
+__device__ __forceinline__ float ld_state1(const float* p) {
+  if constexpr (USE) {
+    return *p;
+  } else {
+    return 0.0f;
+  }
+}
+template <bool USE>
+__device__ __forceinline__ void st_state1(float* p, float x) {
+  if constexpr (USE) *p = x;
 }
 
 template <int GDT>
@@ -335,8 +376,8 @@ __device__ __forceinline__ void adam8(const Consts& c, const float (&x)[kVec], f
   float* mb = m + e0;
   float* vb = v + e0;
   const f32x4 w0 = ld_f32x4(wb, lane32), w1 = ld_f32x4(wb, lane32 + 16);
-  const f32x4 m0 = ld_f32x4(mb, lane32), m1 = ld_f32x4(mb, lane32 + 16);
-  const f32x4 v0 = ld_f32x4(vb, lane32), v1 = ld_f32x4(vb, lane32 + 16);
+  const f32x4 m0 = ld_state<kUsesM<FORM>>(mb, lane32), m1 = ld_state<kUsesM<FORM>>(mb, lane32 + 16);
+  const f32x4 v0 = ld_state<kUsesV<FORM>>(vb, lane32), v1 = ld_state<kUsesV<FORM>>(vb, lane32 + 16);
   float W[kVec] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
   float M[kVec] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
   float V[kVec] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
@@ -350,10 +391,10 @@ __device__ __forceinline__ void adam8(const Consts& c, const float (&x)[kVec], f
   }
   st_f32x4(wb, lane32, f32x4{W[0], W[1], W[2], W[3]});
   st_f32x4(wb, lane32 + 16, f32x4{W[4], W[5], W[6], W[7]});
-  st_f32x4(mb, lane32, f32x4{M[0], M[1], M[2], M[3]});
-  st_f32x4(mb, lane32 + 16, f32x4{M[4], M[5], M[6], M[7]});
-  st_f32x4(vb, lane32, f32x4{V[0], V[1], V[2], V[3]});
-  st_f32x4(vb, lane32 + 16, f32x4{V[4], V[5], V[6], V[7]});
+  st_state<kUsesM<FORM>>(mb, lane32, f32x4{M[0], M[1], M[2], M[3]});
+  st_state<kUsesM<FORM>>(mb, lane32 + 16, f32x4{M[4], M[5], M[6], M[7]});
+  st_state<kUsesV<FORM>>(vb, lane32, f32x4{V[0], V[1], V[2], V[3]});
+  st_state<kUsesV<FORM>>(vb, lane32 + 16, f32x4{V[4], V[5], V[6], V[7]});
   if constexpr (PARAM)
     st_u16x8(par + e0, lane16,
              u32x4{narrow2<PDT>(W[0], W[1]), narrow2<PDT>(W[2], W[3]), narrow2<PDT>(W[4], W[5]),
@@ -373,10 +414,10 @@ __device__ __forceinline__ void adam8x2(const Consts& c, const float (&a)[kVec],
     const int64_t e = q == 0 ? e0 : e1;
     S[q][0] = ld_f32x4(w + e, lane32);
     S[q][1] = ld_f32x4(w + e, lane32 + 16);
-    S[q][2] = ld_f32x4(m + e, lane32);
-    S[q][3] = ld_f32x4(m + e, lane32 + 16);
-    S[q][4] = ld_f32x4(v + e, lane32);
-    S[q][5] = ld_f32x4(v + e, lane32 + 16);
+    S[q][2] = ld_state<kUsesM<FORM>>(m + e, lane32);
+    S[q][3] = ld_state<kUsesM<FORM>>(m + e, lane32 + 16);
+    S[q][4] = ld_state<kUsesV<FORM>>(v + e, lane32);
+    S[q][5] = ld_state<kUsesV<FORM>>(v + e, lane32 + 16);
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -393,10 +434,10 @@ __device__ __forceinline__ void adam8x2(const Consts& c, const float (&a)[kVec],
     for (int j = 0; j < kVec; ++j) adam1<FORM>(c, x[j] / c.PF, W[j], M[j], V[j]);
     st_f32x4(w + e, lane32, f32x4{W[0], W[1], W[2], W[3]});
     st_f32x4(w + e, lane32 + 16, f32x4{W[4], W[5], W[6], W[7]});
-    st_f32x4(m + e, lane32, f32x4{M[0], M[1], M[2], M[3]});
-    st_f32x4(m + e, lane32 + 16, f32x4{M[4], M[5], M[6], M[7]});
-    st_f32x4(v + e, lane32, f32x4{V[0], V[1], V[2], V[3]});
-    st_f32x4(v + e, lane32 + 16, f32x4{V[4], V[5], V[6], V[7]});
+    st_state<kUsesM<FORM>>(m + e, lane32, f32x4{M[0], M[1], M[2], M[3]});
+    st_state<kUsesM<FORM>>(m + e, lane32 + 16, f32x4{M[4], M[5], M[6], M[7]});
+    st_state<kUsesV<FORM>>(v + e, lane32, f32x4{V[0], V[1], V[2], V[3]});
+    st_state<kUsesV<FORM>>(v + e, lane32 + 16, f32x4{V[4], V[5], V[6], V[7]});
     st_u16x8(par + e, lane16,
              u32x4{narrow2<PDT>(W[0], W[1]), narrow2<PDT>(W[2], W[3]), narrow2<PDT>(W[4], W[5]),
                    narrow2<PDT>(W[6], W[7])});
@@ -443,11 +484,11 @@ __device__ __forceinline__ void fused_rest(const Grads& gr, int p, float* __rest
     for (int64_t i = tid; i < nsc; i += kBlock) {
       const int64_t e = i < h ? i : t0 + (i - h);
       const float g = mean1<GDT>(gr, p, e, c.PF);
-      float W = w[e], M = m[e], V = v[e];
+      float W = w[e], M = ld_state1<kUsesM<FORM>>(m + e), V = ld_state1<kUsesV<FORM>>(v + e);
       adam1<FORM>(c, g, W, M, V);
       w[e] = W;
-      m[e] = M;
-      v[e] = V;
+      st_state1<kUsesM<FORM>>(m + e, M);
+      st_state1<kUsesV<FORM>>(v + e, V);
       par[e] = narrow1<PDT>(W);
     }
   }
@@ -599,10 +640,10 @@ void table_kernel(TableSrc src, int p, Consts c) {
           const int64_t e0 = h + (g0 + static_cast<int64_t>(u0 + q) * kBlock) * kVec;
           A[q][0] = ld_f32x4(w + e0, lane32);
           A[q][1] = ld_f32x4(w + e0, lane32 + 16);
-          A[q][2] = ld_f32x4(m + e0, lane32);
-          A[q][3] = ld_f32x4(m + e0, lane32 + 16);
-          A[q][4] = ld_f32x4(v + e0, lane32);
-          A[q][5] = ld_f32x4(v + e0, lane32 + 16);
+          A[q][2] = ld_state<kUsesM<FORM>>(m + e0, lane32);
+          A[q][3] = ld_state<kUsesM<FORM>>(m + e0, lane32 + 16);
+          A[q][4] = ld_state<kUsesV<FORM>>(v + e0, lane32);
+          A[q][5] = ld_state<kUsesV<FORM>>(v + e0, lane32 + 16);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -616,10 +657,10 @@ void table_kernel(TableSrc src, int p, Consts c) {
           for (int j = 0; j < kVec; ++j) adam1<FORM>(c, s[u][j] / c.PF, W[j], M[j], V[j]);
           st_f32x4(w + e0, lane32, f32x4{W[0], W[1], W[2], W[3]});
           st_f32x4(w + e0, lane32 + 16, f32x4{W[4], W[5], W[6], W[7]});
-          st_f32x4(m + e0, lane32, f32x4{M[0], M[1], M[2], M[3]});
-          st_f32x4(m + e0, lane32 + 16, f32x4{M[4], M[5], M[6], M[7]});
-          st_f32x4(v + e0, lane32, f32x4{V[0], V[1], V[2], V[3]});
-          st_f32x4(v + e0, lane32 + 16, f32x4{V[4], V[5], V[6], V[7]});
+          st_state<kUsesM<FORM>>(m + e0, lane32, f32x4{M[0], M[1], M[2], M[3]});
+          st_state<kUsesM<FORM>>(m + e0, lane32 + 16, f32x4{M[4], M[5], M[6], M[7]});
+          st_state<kUsesV<FORM>>(v + e0, lane32, f32x4{V[0], V[1], V[2], V[3]});
+          st_state<kUsesV<FORM>>(v + e0, lane32 + 16, f32x4{V[4], V[5], V[6], V[7]});
           st_u16x8(par + e0, lane16,
                    u32x4{narrow2<PDT>(W[0], W[1]), narrow2<PDT>(W[2], W[3]),
                          narrow2<PDT>(W[4], W[5]), narrow2<PDT>(W[6], W[7])});
@@ -716,8 +757,8 @@ void fused_kernel(GradArgs<PMAX> ga, int p, float* __restrict__ w, float* __rest
       float* mb = m + e0;
       float* vb = v + e0;
       const f32x4 w0 = ld_f32x4(wb, lane32), w1 = ld_f32x4(wb, lane32 + 16);
-      const f32x4 m0 = ld_f32x4(mb, lane32), m1 = ld_f32x4(mb, lane32 + 16);
-      const f32x4 v0 = ld_f32x4(vb, lane32), v1 = ld_f32x4(vb, lane32 + 16);
+      const f32x4 m0 = ld_state<kUsesM<FORM>>(mb, lane32), m1 = ld_state<kUsesM<FORM>>(mb, lane32 + 16);
+      const f32x4 v0 = ld_state<kUsesV<FORM>>(vb, lane32), v1 = ld_state<kUsesV<FORM>>(vb, lane32 + 16);
       float W[kVec] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
       float M[kVec] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
       float V[kVec] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
@@ -725,10 +766,10 @@ void fused_kernel(GradArgs<PMAX> ga, int p, float* __restrict__ w, float* __rest
       for (int j = 0; j < kVec; ++j) adam1<FORM>(c, s[u][j] / c.PF, W[j], M[j], V[j]);
       st_f32x4(wb, lane32, f32x4{W[0], W[1], W[2], W[3]});
       st_f32x4(wb, lane32 + 16, f32x4{W[4], W[5], W[6], W[7]});
-      st_f32x4(mb, lane32, f32x4{M[0], M[1], M[2], M[3]});
-      st_f32x4(mb, lane32 + 16, f32x4{M[4], M[5], M[6], M[7]});
-      st_f32x4(vb, lane32, f32x4{V[0], V[1], V[2], V[3]});
-      st_f32x4(vb, lane32 + 16, f32x4{V[4], V[5], V[6], V[7]});
+      st_state<kUsesM<FORM>>(mb, lane32, f32x4{M[0], M[1], M[2], M[3]});
+      st_state<kUsesM<FORM>>(mb, lane32 + 16, f32x4{M[4], M[5], M[6], M[7]});
+      st_state<kUsesV<FORM>>(vb, lane32, f32x4{V[0], V[1], V[2], V[3]});
+      st_state<kUsesV<FORM>>(vb, lane32 + 16, f32x4{V[4], V[5], V[6], V[7]});
       st_u16x8(par + e0, lane16,
                u32x4{narrow2<PDT>(W[0], W[1]), narrow2<PDT>(W[2], W[3]),
                      narrow2<PDT>(W[4], W[5]), narrow2<PDT>(W[6], W[7])});
@@ -801,11 +842,11 @@ __global__ __launch_bounds__(kBlock) void adam_kernel(const float* __restrict__ 
     const int64_t nsc = h + (len - t0);
     for (int64_t i = tid; i < nsc; i += kBlock) {
       const int64_t e = i < h ? i : t0 + (i - h);
-      float W = w[e], M = m[e], V = v[e];
+      float W = w[e], M = ld_state1<kUsesM<FORM>>(m + e), V = ld_state1<kUsesV<FORM>>(v + e);
       adam1<FORM>(c, gin[e], W, M, V);
       w[e] = W;
-      m[e] = M;
-      v[e] = V;
+      st_state1<kUsesM<FORM>>(m + e, M);
+      st_state1<kUsesV<FORM>>(v + e, V);
       if constexpr (PARAM) par[e] = narrow1<PDT>(W);
     }
   }
@@ -832,13 +873,17 @@ void with_dt(int dt, F&& f) {
 
 template <class F>
 void with_form(int form, F&& f) {
-  if (form == kStandard) f(IC<kStandard>{}); else f(IC<kPage1Literal>{});
+  switch (form) {
+    case kStandard: f(IC<kStandard>{}); break;
+    case kPage1Literal: f(IC<kPage1Literal>{}); break;
+    case kSgd: f(IC<kSgd>{}); break;
+    default: f(IC<kSgdMomentum>{}); break;
+  }
 }
 
 template <class F>
 void with_pmax(int p, F&& f) {
-  if (p <= 8) f(IC<8>{});
-  else if (p <= 64) f(IC<64>{});
+  if (p <= 64) f(IC<64>{});
   else f(IC<256>{});
 }
 

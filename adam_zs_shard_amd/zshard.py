@@ -17,10 +17,16 @@ LIB_PATH = os.path.join(HERE, "libzshard.so")
 ZS_OK, ZS_ERR_NULL, ZS_ERR_ARG, ZS_ERR_DTYPE, ZS_ERR_RANGE, ZS_ERR_ALIAS, ZS_ERR_CAPACITY, \
     ZS_ERR_HIP = range(8)
 ZS_F16, ZS_BF16 = 1, 2
-ZS_ADAM_STANDARD, ZS_ADAM_PAGE1_LITERAL = 0, 1
+ZS_ADAM_STANDARD, ZS_ADAM_PAGE1_LITERAL, ZS_SGD, ZS_SGD_MOMENTUM = 0, 1, 2, 3
+ZS_STATE_M, ZS_STATE_V = 1, 2
 ZS_MAX_P = 256
 
-FORMS = {"standard": ZS_ADAM_STANDARD, "page1_literal": ZS_ADAM_PAGE1_LITERAL}
+FORMS = {"standard": ZS_ADAM_STANDARD, "page1_literal": ZS_ADAM_PAGE1_LITERAL, "sgd": ZS_SGD,
+         "sgd_momentum": ZS_SGD_MOMENTUM}
+# bytes per element of one step at p ranks, by form (gradients, state read and
+# written, the 16-bit working copy)
+BYTES_PER_ELEM = {ZS_ADAM_STANDARD: 26, ZS_ADAM_PAGE1_LITERAL: 26, ZS_SGD: 10,
+                  ZS_SGD_MOMENTUM: 18}
 DTYPE_NAMES = {"f16": ZS_F16, "bf16": ZS_BF16}
 
 
@@ -60,7 +66,7 @@ class zs_piece_ptrs(C.Structure):
 class zs_mt_table(C.Structure):
     _fields_ = [("workspace", C.c_void_p), ("nchunks", C.c_int64), ("chunk_elems", C.c_int64),
                 ("npieces", C.c_int32), ("p", C.c_int32), ("grad_dtype", C.c_int32),
-                ("param_dtype", C.c_int32)]
+                ("param_dtype", C.c_int32), ("state", C.c_int32), ("reserved", C.c_int32)]
 
 
 EXPORTS = [

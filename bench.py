@@ -45,9 +45,10 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
+def measured_traffic(workload: str, form: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, or None if
-    there are none for this workload or the kernel sources changed since."""
+    there are none for this workload and update form, or the kernel sources
+    changed since."""
     try:
         with open(COUNTERS_FILE) as fh:
             data = json.load(fh)
@@ -55,6 +56,8 @@ def measured_traffic(workload: str):
         return None
     rec = data.get(workload)
     if not rec or rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    if rec.get("form", "standard") != form:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -110,6 +113,24 @@ def host_threads() -> int:
     return max(1, min(16, n))
 
 
+def _state(wl, w):
+    """(m, v) for the workload's form: None where the form uses no such state."""
+    import torch
+
+    from adam_zs_shard_amd import zshard as z
+
+    f = z.FORMS[wl.form]
+    m = torch.zeros_like(w) if f != z.ZS_SGD else None
+    v = torch.zeros_like(w) if f in (z.ZS_ADAM_STANDARD, z.ZS_ADAM_PAGE1_LITERAL) else None
+    return m, v
+
+
+def _bytes_per_elem(wl):
+    from adam_zs_shard_amd import zshard as z
+
+    return 2 * wl.p + z.BYTES_PER_ELEM[z.FORMS[wl.form]]
+
+
 def bench_single(args):
     """Fused single-tensor step on one shard with P separate gradient slices."""
     import numpy as np
@@ -129,8 +150,7 @@ def bench_single(args):
     grads = [normal(L, wl.grad_std, seed_for(20261202, r, 1, 1, k), td[wl.grad_dtype], dev)
              for r in range(wl.p)]
     w = normal(L, wl.w_std, seed_for(20261202, -1, 0, 2, k), torch.float32, dev)
-    m = torch.zeros_like(w)
-    v = torch.zeros_like(w)
+    m, v = _state(wl, w)
     if wl.param_layout == "full":
         param = torch.empty(wl.n, dtype=td[wl.param_dtype], device=dev)
         pbase = 0
@@ -148,7 +168,7 @@ def bench_single(args):
                               grad_base=gbase, param_base=pbase, stream=stream.cuda_stream)
 
     ms, wall = _time_steps(step, args.steps, args.warmup, stream)
-    bytes_per_elem = 2 * wl.p + 26
+    bytes_per_elem = _bytes_per_elem(wl)
     launches_per_step = 1
     elems = L
 
@@ -158,8 +178,8 @@ def bench_single(args):
         a0 = (L - S) // 2
         gh = [g[a0:a0 + S].view(torch.int16).cpu().numpy().view(np.uint16) for g in grads]
         wh = w[a0:a0 + S].cpu().numpy().copy()
-        mh = m[a0:a0 + S].cpu().numpy().copy()
-        vh = v[a0:a0 + S].cpu().numpy().copy()
+        mh = m[a0:a0 + S].cpu().numpy().copy() if m is not None else np.zeros(S, np.float32)
+        vh = v[a0:a0 + S].cpu().numpy().copy() if v is not None else np.zeros(S, np.float32)
         thr = host_threads()
         secs = cpu_baseline(wl.grad_dtype, wl.param_dtype, gh, wh, mh, vh, thr, wl.form)
         cpu = {"value": S / secs, "unit": "elements/s", "cores": thr, "kind": "oracle",
@@ -179,8 +199,8 @@ def _cpu_leg(args, wl, grads, w, m, v, label):
     a0 = (L - S) // 2
     gh = [g[a0:a0 + S].view(torch.int16).cpu().numpy().view(np.uint16) for g in grads]
     wh = w[a0:a0 + S].cpu().numpy().copy()
-    mh = m[a0:a0 + S].cpu().numpy().copy()
-    vh = v[a0:a0 + S].cpu().numpy().copy()
+    mh = m[a0:a0 + S].cpu().numpy().copy() if m is not None else np.zeros(S, np.float32)
+    vh = v[a0:a0 + S].cpu().numpy().copy() if v is not None else np.zeros(S, np.float32)
     thr = host_threads()
     secs = cpu_baseline(wl.grad_dtype, wl.param_dtype, gh, wh, mh, vh, thr, wl.form)
     return {"value": S / secs, "unit": "elements/s", "cores": thr, "kind": "oracle",
@@ -212,13 +232,15 @@ def bench_multi(args):
           f"chunks={nchunks} chunk_elems={args.chunk}", file=sys.stderr, flush=True)
     grads = [make.normal_grad(wl, r, 1, L, dev, stream=k) for r in range(wl.p)]
     w = make.initial_w(wl, k, L, dev)
-    m = torch.zeros_like(w)
-    v = torch.zeros_like(w)
+    m, v = _state(wl, w)
     params = {}
     for (t, _, _, _) in pieces:
         if t not in params:
             params[t] = torch.empty(numel[t], dtype=td[wl.param_dtype], device=dev)
-    ptrs = [dict(w=w.data_ptr() + 4 * so, m=m.data_ptr() + 4 * so, v=v.data_ptr() + 4 * so,
+    def at(x, off):
+        return None if x is None else x.data_ptr() + off
+
+    ptrs = [dict(w=at(w, 4 * so), m=at(m, 4 * so), v=at(v, 4 * so),
                  param=params[t].data_ptr() + 2 * to, grads=[g.data_ptr() + 2 * so for g in grads])
             for (t, to, so, ln) in pieces]
     nb = z.zs_mt_workspace_bytes(len(pieces), nchunks, wl.p)
@@ -234,9 +256,9 @@ def bench_multi(args):
 
     ms, wall = _time_steps(step, args.steps, args.warmup, stream)
     cpu = None if args.no_cpu_baseline else _cpu_leg(args, wl, grads, w, m, v, f"shard {k}")
-    return dict(wl=wl, k=k, elems=L, ms=ms, wall=wall, bytes_per_elem=2 * wl.p + 26, launches=1,
-                launch_elems=L, cpu=cpu, extra={"pieces": len(pieces), "chunks": nchunks,
-                                                "chunk_elems": args.chunk})
+    return dict(wl=wl, k=k, elems=L, ms=ms, wall=wall, bytes_per_elem=_bytes_per_elem(wl),
+                launches=1, launch_elems=L, cpu=cpu,
+                extra={"pieces": len(pieces), "chunks": nchunks, "chunk_elems": args.chunk})
 
 
 def bench_all_shards(args):
@@ -261,7 +283,7 @@ def bench_all_shards(args):
     states = []
     for k in range(wl.p):
         w = make.initial_w(wl, k, e[k] - s[k], dev)
-        states.append((w, torch.zeros_like(w), torch.zeros_like(w)))
+        states.append((w,) + _state(wl, w))
     param = torch.empty(wl.n, dtype=td[wl.param_dtype], device=dev)
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
@@ -279,7 +301,7 @@ def bench_all_shards(args):
     if not args.no_cpu_baseline:
         w, m, v = states[k0]
         cpu = _cpu_leg(args, wl, [g[s[k0]:e[k0]] for g in grads], w, m, v, f"shard {k0}")
-    return dict(wl=wl, k=None, elems=wl.n, ms=ms, wall=wall, bytes_per_elem=2 * wl.p + 26,
+    return dict(wl=wl, k=None, elems=wl.n, ms=ms, wall=wall, bytes_per_elem=_bytes_per_elem(wl),
                 launches=wl.p, launch_elems=wl.n / wl.p, cpu=cpu,
                 extra={"launches_per_step": wl.p})
 
@@ -311,6 +333,9 @@ def main():
     ap.add_argument("--workload", default="zero_7p5b_p64")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=1 << 25)
+    ap.add_argument("--form", default=None,
+                    choices=["standard", "page1_literal", "sgd", "sgd_momentum"],
+                    help="override the workload's update form (bytes per element follow it)")
     ap.add_argument("--chunk", type=int, default=0,
                     help="chunk-table chunk length in elements (multi-tensor workloads); 0 picks "
                          "one whole kernel chunk (57,344), or for shards under two of those per "
@@ -340,6 +365,10 @@ def main():
     if args.workload not in WORKLOADS:
         print(f"unknown workload {args.workload}; one of {sorted(WORKLOADS)}", file=sys.stderr)
         sys.exit(2)
+    if args.form is not None:
+        import dataclasses
+
+        WORKLOADS[args.workload] = dataclasses.replace(WORKLOADS[args.workload], form=args.form)
     wlx = WORKLOADS[args.workload]
     if wlx.param_layout == "tensors":
         r = bench_multi(args)
@@ -353,7 +382,7 @@ def main():
     launch_ms = ms / r["launches"]
     alg_bytes = r["bytes_per_elem"] * r["launch_elems"]
     gbs = alg_bytes / (launch_ms / 1e3) / 1e9
-    traffic = measured_traffic(wl.name)
+    traffic = measured_traffic(wl.name, wl.form)
     out = {
         "metric": METRIC,
         "value": elems_per_s,

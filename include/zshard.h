@@ -70,7 +70,22 @@ typedef enum { ZS_F16 = 1, ZS_BF16 = 2 } zs_dtype;
  * ([ZA] §1.1.1; Kingma & Ba, its ref. 10).  The page-1 literal form stores
  * the corrected moments m_{t+1} = (b1 m_t + (1-b1) g)/(1 - b1^{t+1}) and
  * likewise v ([DP-III] §(一)); it is not equivalent to standard Adam. */
-typedef enum { ZS_ADAM_STANDARD = 0, ZS_ADAM_PAGE1_LITERAL = 1 } zs_adam_form;
+/* The update applied after the rank mean g.  The two Adam forms read and
+ * write w, m, v; the SGD forms leave the state they do not use untouched, and
+ * its pointers may then be NULL (m and v for ZS_SGD, v for ZS_SGD_MOMENTUM).
+ *  ZS_SGD:          w = w - lr*g  ([DP-III] §(一), the SGD update); 2P + 10
+ *                   bytes per element instead of 2P + 26.
+ *  ZS_SGD_MOMENTUM: m = beta1*m + g; w = w - lr*m.  [ZA] §1.1.1 names SGD
+ *                   with momentum and its stored buffer without a formula:
+ *                   this is the heavy-ball form, coefficient beta1; 2P + 18
+ *                   bytes per element.
+ * beta2 and eps are validated but unused by the SGD forms. */
+typedef enum {
+  ZS_ADAM_STANDARD = 0,
+  ZS_ADAM_PAGE1_LITERAL = 1,
+  ZS_SGD = 2,
+  ZS_SGD_MOMENTUM = 3
+} zs_adam_form;
 
 typedef struct {
   double lr;     /* learning rate, finite */
@@ -101,7 +116,8 @@ zs_status zs_plan_shards(int64_t n, int32_t p, int64_t* m_out, int64_t* starts, 
  *     grad_base + i.  grad_base = 0 for full-length buffers, = s_k for buffers
  *     that hold only this shard.  Read only.  dtype grad_dtype.
  *  w, m, v: fp32, e_k - s_k elements each, element i = global s_k + i,
- *     updated in place.  m0 = v0 = 0 at step 1 ([DP-III] §(一)).
+ *     updated in place.  m0 = v0 = 0 at step 1 ([DP-III] §(一)).  m and v
+ *     may be NULL for a form that does not use them (see zs_adam_form).
  *  param: the 16-bit working copy; param[j - param_base] is written for each
  *     j in [s_k, e_k) and nothing else.  param_base = 0 for a full-length
  *     working copy (this rank's contribution to the all-gather).
@@ -124,13 +140,14 @@ typedef struct {
 } zs_shard_args;
 
 /* The whole step in one kernel: gather + rank-order mean + Adam + downcast.
- * Memory traffic per element: 2p (grads) + 12 (w, m, v read) + 12 (write)
- * + 2 (param) bytes.  The fp32 mean is never stored ([DP-III] §(三) step 4:
+ * Memory traffic per element (Adam): 2p (grads) + 12 (w, m, v read) + 12
+ * (write) + 2 (param) bytes; 2p + 10 for ZS_SGD, 2p + 18 for
+ * ZS_SGD_MOMENTUM.  The fp32 mean is never stored ([DP-III] §(三) step 4:
  * the gradient is released after the update).
- * Errors: ZS_ERR_NULL (args, hp, grads, any grads[r], w, m, v, param when
- * the shard is non-empty), ZS_ERR_ARG, ZS_ERR_DTYPE, ZS_ERR_RANGE,
- * ZS_ERR_ALIAS (w, m, v, param overlap each other or any gradient range),
- * ZS_ERR_HIP. */
+ * Errors: ZS_ERR_NULL (args, hp, grads, any grads[r], w, param, or m / v
+ * when the form uses them, when the shard is non-empty), ZS_ERR_ARG,
+ * ZS_ERR_DTYPE, ZS_ERR_RANGE, ZS_ERR_ALIAS (the buffers the form writes
+ * overlap each other or any gradient range), ZS_ERR_HIP. */
 zs_status zs_fused_shard_step(const zs_shard_args* args);
 
 /* The gradient mean alone, stored (the local stand-in for reduce-scatter +
@@ -178,7 +195,8 @@ zs_status zs_plan_chunks(const int64_t* numel, int32_t ntensors, int32_t p, int3
 
 /* Device pointers of one piece, each already at the piece's first element:
  * w/m/v fp32, param 16-bit, grads[r] the 16-bit gradient of rank r (host
- * array of p device pointers). */
+ * array of p device pointers).  m and v may be NULL; a step whose form needs
+ * them then fails with ZS_ERR_NULL unless every piece has them. */
 typedef struct {
   float* w;
   float* m;
@@ -196,7 +214,12 @@ typedef struct {
   int32_t p;
   int32_t grad_dtype;
   int32_t param_dtype;
+  int32_t state;    /* ZS_STATE_M | ZS_STATE_V: every piece has that buffer */
+  int32_t reserved;
 } zs_mt_table;
+
+#define ZS_STATE_M 1
+#define ZS_STATE_V 2
 
 /* Bytes of device workspace that zs_mt_upload needs (0 on bad arguments). */
 size_t zs_mt_workspace_bytes(int32_t npieces, int64_t nchunks, int32_t p);

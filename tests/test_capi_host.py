@@ -125,7 +125,8 @@ def test_fused_argument_errors():
     assert _fused(hp=z.hparams(1e-3, 1.0, 0.999, 1e-8, 1)) == z.ZS_ERR_ARG
     assert _fused(hp=z.hparams(float("nan"), 0.9, 0.999, 1e-8, 1)) == z.ZS_ERR_ARG
     assert _fused(hp=z.hparams(1e-3, 0.9, 0.999, float("inf"), 1)) == z.ZS_ERR_ARG
-    assert _fused(hp=z.hparams(1e-3, 0.9, 0.999, 1e-8, 1, form=2)) == z.ZS_ERR_ARG
+    assert _fused(hp=z.hparams(1e-3, 0.9, 0.999, 1e-8, 1, form=4)) == z.ZS_ERR_ARG
+    assert _fused(hp=z.hparams(1e-3, 0.9, 0.999, 1e-8, 1, form=-1)) == z.ZS_ERR_ARG
     assert _fused(w=None) == z.ZS_ERR_NULL
     assert _fused(param=None) == z.ZS_ERR_NULL
     assert _fused(grads=[FAKE, None, FAKE, FAKE]) == z.ZS_ERR_NULL
@@ -211,8 +212,14 @@ def test_mt_upload_argument_errors():
     bad[1]["param"] = FAKE + (4 << 30) + 100     # param on top of a gradient
     assert up(ptrs=bad) == z.ZS_ERR_ALIAS
     bad = [dict(ptrs[0]), dict(ptrs[1])]
-    bad[0]["v"] = None
+    bad[0]["w"] = None
     assert up(ptrs=bad) == z.ZS_ERR_NULL
+    # m and v are optional at upload (the step checks the form against the
+    # table's state mask); passing the checks means reaching the copy, which
+    # fails with ZS_ERR_HIP on a host without a device
+    nov = [dict(ptrs[0]), dict(ptrs[1])]
+    nov[0]["v"] = None
+    assert up(ptrs=nov) == z.ZS_ERR_HIP
 
 
 @no_device
@@ -229,3 +236,42 @@ def test_multi_step_argument_errors():
     t.grad_dtype = 1
     assert z.zs_fused_shard_step_multi(t, z.hparams(1e-3, 0.9, 0.999, 1e-8, 0),
                                        check=False) == z.ZS_ERR_ARG
+
+
+@no_device
+def test_state_pointers_required_by_form():
+    # Adam needs m and v, momentum SGD only m, plain SGD neither.  On a host
+    # with no device, ZS_ERR_HIP means every check before the launch passed.
+    adam = z.hparams(1e-3, 0.9, 0.999, 1e-8, 1, "standard")
+    lit = z.hparams(1e-3, 0.9, 0.999, 1e-8, 1, "page1_literal")
+    sgd = z.hparams(1e-3, 0.9, 0.999, 1e-8, 1, "sgd")
+    mom = z.hparams(1e-3, 0.9, 0.999, 1e-8, 1, "sgd_momentum")
+    for hp in (adam, lit):
+        assert _fused(hp=hp, m=None) == z.ZS_ERR_NULL
+        assert _fused(hp=hp, v=None) == z.ZS_ERR_NULL
+    assert _fused(hp=mom, m=None) == z.ZS_ERR_NULL
+    assert _fused(hp=mom, v=None) == z.ZS_ERR_HIP
+    assert _fused(hp=sgd, m=None, v=None) == z.ZS_ERR_HIP
+    # state a form does not use is not written, so it may even alias w
+    assert _fused(hp=sgd, m=FAKE, v=FAKE) == z.ZS_ERR_HIP
+    assert _fused(hp=mom, m=FAKE) == z.ZS_ERR_ALIAS
+    assert z.zs_adam_step(FAKE, FAKE + (1 << 30), None, None, None, 100, sgd,
+                          check=False) == z.ZS_ERR_HIP
+    assert z.zs_adam_step(FAKE, FAKE + (1 << 30), None, None, None, 100, mom,
+                          check=False) == z.ZS_ERR_NULL
+
+
+@no_device
+def test_multi_step_checks_state_mask():
+    def step(state, form):
+        t = z.zs_mt_table(workspace=FAKE, nchunks=4, chunk_elems=64, npieces=1, p=2,
+                          grad_dtype=1, param_dtype=1, state=state)
+        return z.zs_fused_shard_step_multi(t, z.hparams(1e-3, 0.9, 0.999, 1e-8, 1, form),
+                                           check=False)
+    both = z.ZS_STATE_M | z.ZS_STATE_V
+    assert step(both, "standard") == z.ZS_ERR_HIP          # checks passed
+    assert step(z.ZS_STATE_M, "standard") == z.ZS_ERR_NULL
+    assert step(z.ZS_STATE_M, "page1_literal") == z.ZS_ERR_NULL
+    assert step(z.ZS_STATE_M, "sgd_momentum") == z.ZS_ERR_HIP
+    assert step(0, "sgd_momentum") == z.ZS_ERR_NULL
+    assert step(0, "sgd") == z.ZS_ERR_HIP
