@@ -23,6 +23,12 @@ COMMON = [
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 SOURCES = ["zs_kernels.hip", "zs_capi.cpp"]
+# Host-only code (the CPU offload update), compiled as plain C++: SIMD code
+# paths are selected per function with target attributes.
+HOST_SOURCES = ["zs_cpu.cpp"]
+CXX = os.environ.get("CXX_HOST", "g++")
+HOST = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-ffp-contract=off", "-fno-fast-math",
+        "-I", os.path.join(ROOT, "include")]
 
 
 def build(verbose: bool = True) -> str:
@@ -35,8 +41,15 @@ def build(verbose: bool = True) -> str:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
         objs.append(obj)
+    for src in HOST_SOURCES:
+        obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
+        cmd = [CXX, *HOST, "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        objs.append(obj)
     tmp = LIB_PATH + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

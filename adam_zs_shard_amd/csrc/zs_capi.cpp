@@ -107,6 +107,7 @@ const char* zs_status_string(int32_t status) {
     case ZS_ERR_ALIAS: return "ZS_ERR_ALIAS";
     case ZS_ERR_CAPACITY: return "ZS_ERR_CAPACITY";
     case ZS_ERR_HIP: return "ZS_ERR_HIP";
+    case ZS_ERR_UNSUPPORTED: return "ZS_ERR_UNSUPPORTED";
     default: return "ZS_ERR_UNKNOWN";
   }
 }

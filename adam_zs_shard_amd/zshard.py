@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libzshard.so")
 
 ZS_OK, ZS_ERR_NULL, ZS_ERR_ARG, ZS_ERR_DTYPE, ZS_ERR_RANGE, ZS_ERR_ALIAS, ZS_ERR_CAPACITY, \
-    ZS_ERR_HIP = range(8)
+    ZS_ERR_HIP, ZS_ERR_UNSUPPORTED = range(9)
 ZS_F16, ZS_BF16 = 1, 2
 ZS_ADAM_STANDARD, ZS_ADAM_PAGE1_LITERAL, ZS_SGD, ZS_SGD_MOMENTUM = 0, 1, 2, 3
 ZS_STATE_M, ZS_STATE_V = 1, 2
@@ -72,7 +72,7 @@ class zs_mt_table(C.Structure):
 EXPORTS = [
     "zs_status_string", "zs_version", "zs_last_hip_error", "zs_plan_shards",
     "zs_fused_shard_step", "zs_reduce_scatter_mean_local", "zs_adam_step", "zs_plan_chunks",
-    "zs_mt_workspace_bytes", "zs_mt_upload", "zs_fused_shard_step_multi",
+    "zs_mt_workspace_bytes", "zs_mt_upload", "zs_fused_shard_step_multi", "zs_cpu_adam_step",
 ]
 
 _lib = None
@@ -111,6 +111,9 @@ def lib():
         L.zs_fused_shard_step_multi.argtypes = [C.POINTER(zs_mt_table),
                                                 C.POINTER(zs_adam_hparams), vp]
         L.zs_fused_shard_step_multi.restype = i32
+        L.zs_cpu_adam_step.argtypes = [vp, i32, vp, vp, vp, vp, i32, i64,
+                                       C.POINTER(zs_adam_hparams), i32]
+        L.zs_cpu_adam_step.restype = i32
         _lib = L
     return _lib
 
@@ -273,4 +276,30 @@ def zs_fused_shard_step_multi(table: zs_mt_table, hp: zs_adam_hparams, *, stream
     st = lib().zs_fused_shard_step_multi(C.byref(table), C.byref(hp), _stream(stream))
     if check:
         _check(st, "zs_fused_shard_step_multi")
+    return st
+
+
+def _host_addr(x) -> int | None:
+    """Address of a host numpy array or CPU tensor (or an int / None)."""
+    if x is None or isinstance(x, int):
+        return x
+    if hasattr(x, "ctypes"):
+        return x.ctypes.data
+    if x.is_cuda:
+        raise ValueError("zs_cpu_adam_step takes host memory")
+    return x.data_ptr()
+
+
+def zs_cpu_adam_step(g, grad_dtype, w, m, v, param, param_dtype, length: int,
+                     hp: zs_adam_hparams, *, threads: int = 0, check=True) -> int:
+    """The update of one shard on the host CPU (optimizer offload); every
+    buffer is host memory (numpy arrays or CPU tensors).  grad_dtype /
+    param_dtype: "f16", "bf16" or the zs_dtype value."""
+    gdt = DTYPE_NAMES[grad_dtype] if isinstance(grad_dtype, str) else int(grad_dtype)
+    pdt = 0 if param is None else (DTYPE_NAMES[param_dtype] if isinstance(param_dtype, str)
+                                   else int(param_dtype))
+    st = lib().zs_cpu_adam_step(_host_addr(g), gdt, _host_addr(w), _host_addr(m), _host_addr(v),
+                                _host_addr(param), pdt, length, C.byref(hp), threads)
+    if check:
+        _check(st, "zs_cpu_adam_step")
     return st

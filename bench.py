@@ -306,6 +306,70 @@ def bench_all_shards(args):
                 extra={"launches_per_step": wl.p})
 
 
+def bench_cpu_offload(args):
+    """The optimizer-offload update of one shard on the host CPU: the shard's
+    16-bit gradient, fp32 w/m/v and the 16-bit copy all in host memory; the
+    roofline is host memory bandwidth, taken from a multithreaded in-place
+    pass over 2 GiB timed in the same run."""
+    import numpy as np
+    import torch
+
+    from adam_zs_shard_amd import zshard as z
+    from zs_synth import WORKLOADS, make
+
+    wl = WORKLOADS[args.workload]
+    k = wl.shards[-1]
+    M, s, e = z.zs_plan_shards(wl.n, wl.p)
+    L = e[k] - s[k]
+    thr = host_threads()
+    torch.set_num_threads(thr)
+    print(f"[bench] cpu offload {wl.name}: shard {k}, {L} elements, {thr} threads, form {wl.form}",
+          file=sys.stderr, flush=True)
+    g = make.normal_grad(wl, 0, 1, L, "cpu", stream=k).view(torch.int16).numpy().view(np.uint16)
+    w = make.initial_w(wl, k, L, "cpu").numpy().copy()
+    f = z.FORMS[wl.form]
+    m = np.zeros(L, np.float32) if f != z.ZS_SGD else None
+    v = np.zeros(L, np.float32) if f in (z.ZS_ADAM_STANDARD, z.ZS_ADAM_PAGE1_LITERAL) else None
+    par = np.empty(L, np.uint16)
+    gdt = wl.grad_dtype
+
+    def step(i):
+        z.zs_cpu_adam_step(g, gdt, w, m, v, par, wl.param_dtype, L,
+                           z.hparams(wl.lr, wl.beta1, wl.beta2, wl.eps, i + 1, wl.form),
+                           threads=thr)
+
+    for i in range(args.warmup):
+        step(i)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    sec = (time.perf_counter() - t0) / args.steps
+    per_elem = 2 + z.BYTES_PER_ELEM[f]   # 2 (16-bit gradient) + state + 2 (16-bit copy)
+    gbs = per_elem * L / sec / 1e9
+    # host ceiling: a multithreaded in-place scale of 2 GiB by exactly 1.0, the
+    # same read-modify-write streaming pattern as the update
+    buf = torch.ones(1 << 29)
+    buf.mul_(1.0)
+    t0 = time.perf_counter()
+    for _ in range(5):
+        buf.mul_(1.0)
+    copy_gbs = 2 * buf.numel() * 4 / ((time.perf_counter() - t0) / 5) / 1e9
+    print(json.dumps({
+        "metric": "shard elements/s and achieved host-memory GB/s, optimizer-offload update on "
+                  "the host CPU",
+        "value": L / sec, "unit": "elements/s", "n_gpus": 0, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": sec * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "shard": k, "elems_per_step": L,
+                   "grad_dtype": wl.grad_dtype, "param_dtype": wl.param_dtype,
+                   "adam_form": wl.form, "threads": thr},
+        "roofline": {"bound": "host_dram", "achieved": gbs, "peak": copy_gbs, "unit": "GB/s",
+                     "frac": gbs / copy_gbs, "traffic": None, "bytes_per_element": per_elem,
+                     "peak_source": f"in-place scale of 2 GiB (torch, {thr} threads), "
+                                    "this run"},
+    }), flush=True)
+
+
 def copy_probe(nbytes: int = 1 << 31, reps: int = 10):
     """A plain device copy of known size (torch's copy kernel), used to
     calibrate rocprofv3's FETCH_SIZE / WRITE_SIZE counters: each dispatch
@@ -340,6 +404,9 @@ def main():
                     help="chunk-table chunk length in elements (multi-tensor workloads); 0 picks "
                          "one whole kernel chunk (57,344), or for shards under two of those per "
                          "CU, the shard split evenly over the CUs (rounded up to 2,048)")
+    ap.add_argument("--cpu-offload", action="store_true",
+                    help="time the host-CPU offload update (zs_cpu_adam_step) of the "
+                         "workload's shard instead of the GPU step; no GPU needed")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain 2 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -350,16 +417,7 @@ def main():
 
     import torch
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    if args.copy_probe:
-        copy_probe()
-        return
     from adam_zs_shard_amd import zshard as z
-
-    z.lib()  # fails loudly if the HIP library is not built
-
     from zs_synth import WORKLOADS
 
     if args.workload not in WORKLOADS:
@@ -369,6 +427,18 @@ def main():
         import dataclasses
 
         WORKLOADS[args.workload] = dataclasses.replace(WORKLOADS[args.workload], form=args.form)
+    if args.cpu_offload:
+        z.lib()  # fails loudly if the library is not built
+        bench_cpu_offload(args)
+        return
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_probe:
+        copy_probe()
+        return
+
+    z.lib()  # fails loudly if the HIP library is not built
     wlx = WORKLOADS[args.workload]
     if wlx.param_layout == "tensors":
         r = bench_multi(args)

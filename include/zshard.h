@@ -61,7 +61,8 @@ typedef enum {
   ZS_ERR_RANGE = 4,    /* a base index lies past the shard start, or a size overflows */
   ZS_ERR_ALIAS = 5,    /* an output range overlaps another input or output range */
   ZS_ERR_CAPACITY = 6, /* a caller-provided table or workspace is too small */
-  ZS_ERR_HIP = 7       /* a HIP call failed; see zs_last_hip_error() */
+  ZS_ERR_HIP = 7,      /* a HIP call failed; see zs_last_hip_error() */
+  ZS_ERR_UNSUPPORTED = 8 /* the host CPU lacks an instruction set the call needs */
 } zs_status;
 
 typedef enum { ZS_F16 = 1, ZS_BF16 = 2 } zs_dtype;
@@ -248,6 +249,27 @@ zs_status zs_mt_upload(const zs_piece* pieces, const zs_piece_ptrs* ptrs, int32_
  * ZS_ERR_DTYPE, ZS_ERR_HIP. */
 zs_status zs_fused_shard_step_multi(const zs_mt_table* table, const zs_adam_hparams* hp,
                                     void* stream);
+
+/* ---- optimizer offload: the update on the host CPU -----------------------
+ * [ZA] §2.2 Offload 策略: the GPU sends the shard's 16-bit gradient to host
+ * memory, the CPU keeps the fp32 master weights and moments and runs the
+ * update and the float2half conversion, and the 16-bit parameters go back;
+ * [ZA] §1.6.2: multithreaded SIMD, one CPU process per GPU shard.
+ * All pointers are HOST memory.  g: len 16-bit gradients (grad_dtype), e.g.
+ * the rank mean rounded to 16 bits on the GPU; w, m, v: fp32, updated in
+ * place (m / v may be NULL when the form does not use them, as for
+ * zs_fused_shard_step); param: len 16-bit outputs (param_dtype) or NULL.
+ * Same per-element arithmetic as zs_adam_step applied to the widened
+ * gradient, bit for bit, on 8 lanes at a time (AVX2 + F16C, no FMA), in
+ * `threads` threads (<= 0: all hardware threads; at most one per 64 Ki
+ * elements).  Synchronous; returns when done.  Traffic per element: 2 + 12
+ * + 12 + 2 bytes for Adam (2 + 4 + 4 + 2 for SGD, 2 + 8 + 8 + 2 for momentum).
+ * Errors: ZS_ERR_NULL, ZS_ERR_ARG, ZS_ERR_DTYPE, ZS_ERR_RANGE, ZS_ERR_ALIAS
+ * (the buffers written overlap each other or g), ZS_ERR_UNSUPPORTED (no
+ * AVX2/F16C on this CPU). */
+zs_status zs_cpu_adam_step(const void* g, int32_t grad_dtype, float* w, float* m, float* v,
+                           void* param, int32_t param_dtype, int64_t len,
+                           const zs_adam_hparams* hp, int32_t threads);
 
 #ifdef __cplusplus
 }

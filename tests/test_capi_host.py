@@ -34,7 +34,7 @@ def _declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert len(names) == 11
+    assert len(names) == 12 and sorted(names) == sorted(z.EXPORTS)
     L = z.lib()
     for n in names:
         assert hasattr(L, n), n
