@@ -216,7 +216,7 @@ def bench_multi(args):
     from zs_synth import WORKLOADS, make
 
     wl = WORKLOADS[args.workload]
-    k = wl.shards[0]
+    k = wl.shards[0] if args.shard is None else args.shard
     numel = [n for _, n in wl.tensors]
     M, s, e = z.zs_plan_shards(wl.n, wl.p)
     L = e[k] - s[k]
@@ -243,22 +243,69 @@ def bench_multi(args):
     ptrs = [dict(w=at(w, 4 * so), m=at(m, 4 * so), v=at(v, 4 * so),
                  param=params[t].data_ptr() + 2 * to, grads=[g.data_ptr() + 2 * so for g in grads])
             for (t, to, so, ln) in pieces]
-    nb = z.zs_mt_workspace_bytes(len(pieces), nchunks, wl.p)
-    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    table = z.zs_mt_upload(pieces, ptrs, wl.p, wl.grad_dtype, wl.param_dtype, args.chunk, ws, nb,
-                           stream=stream.cuda_stream)
+    # one table for the whole shard, or (--bucket-elems) one per bucket of
+    # consecutive pieces holding at least that many elements
+    groups, cur, size = [], [], 0
+    for i, pc in enumerate(pieces):
+        cur.append(i)
+        size += pc[3]
+        if args.bucket_elems > 0 and size >= args.bucket_elems:
+            groups.append(cur)
+            cur, size = [], 0
+    if cur:
+        groups.append(cur)
+    tables, keep = [], []
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    for g in groups:
+        sub = [pieces[i] for i in g]
+        chunk = args.chunk
+        if len(groups) > 1:  # a bucket is spread over all CUs on its own
+            lb = sum(pc[3] for pc in sub)
+            chunk = min(args.chunk, max(2048, -(-(-(-lb // ncu)) // 2048) * 2048))
+        nch = sum((ln + chunk - 1) // chunk for (_, _, _, ln) in sub)
+        nb = z.zs_mt_workspace_bytes(len(sub), nch, wl.p)
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        keep.append(ws)
+        tables.append(z.zs_mt_upload(sub, [ptrs[i] for i in g], wl.p, wl.grad_dtype,
+                                     wl.param_dtype, chunk, ws, nb, stream=stream.cuda_stream))
     torch.cuda.synchronize()
 
-    def step(i):
-        z.zs_fused_shard_step_multi(table, z.hparams(wl.lr, wl.beta1, wl.beta2, wl.eps, i + 1,
-                                                     wl.form), stream=stream.cuda_stream)
+    def launches(hp, st):
+        for tb in tables:
+            z.zs_fused_shard_step_multi(tb, hp, stream=st)
+
+    if args.graph:
+        # replay reuses the captured arguments: only forms whose constants do
+        # not change with the step
+        if z.FORMS[wl.form] not in (z.ZS_SGD, z.ZS_SGD_MOMENTUM):
+            print("--graph needs --form sgd or sgd_momentum (Adam's bias corrections change "
+                  "every step)", file=sys.stderr)
+            sys.exit(2)
+        hp0 = z.hparams(wl.lr, wl.beta1, wl.beta2, wl.eps, 1, wl.form)
+        launches(hp0, stream.cuda_stream)   # first call outside capture
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph):
+                launches(hp0, torch.cuda.current_stream().cuda_stream)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+
+        def step(i):
+            graph.replay()
+    else:
+        def step(i):
+            launches(z.hparams(wl.lr, wl.beta1, wl.beta2, wl.eps, i + 1, wl.form),
+                     stream.cuda_stream)
 
     ms, wall = _time_steps(step, args.steps, args.warmup, stream)
     cpu = None if args.no_cpu_baseline else _cpu_leg(args, wl, grads, w, m, v, f"shard {k}")
     return dict(wl=wl, k=k, elems=L, ms=ms, wall=wall, bytes_per_elem=_bytes_per_elem(wl),
-                launches=1, launch_elems=L, cpu=cpu,
-                extra={"pieces": len(pieces), "chunks": nchunks, "chunk_elems": args.chunk})
+                launches=len(tables), launch_elems=L / len(tables), cpu=cpu,
+                extra={"pieces": len(pieces), "chunks": nchunks, "chunk_elems": args.chunk,
+                       "launches_per_step": len(tables), "graph": bool(args.graph)})
 
 
 def bench_all_shards(args):
@@ -404,6 +451,14 @@ def main():
                     help="chunk-table chunk length in elements (multi-tensor workloads); 0 picks "
                          "one whole kernel chunk (57,344), or for shards under two of those per "
                          "CU, the shard split evenly over the CUs (rounded up to 2,048)")
+    ap.add_argument("--shard", type=int, default=None,
+                    help="chunk-table workloads: the rank k whose shard is timed")
+    ap.add_argument("--bucket-elems", type=int, default=0,
+                    help="chunk-table workloads: one launch per bucket of consecutive pieces "
+                         "holding at least this many elements (0: one launch per step)")
+    ap.add_argument("--graph", action="store_true",
+                    help="chunk-table workloads, SGD forms: capture the step's launches in a "
+                         "HIP graph once and time its replays")
     ap.add_argument("--cpu-offload", action="store_true",
                     help="time the host-CPU offload update (zs_cpu_adam_step) of the "
                          "workload's shard instead of the GPU step; no GPU needed")
