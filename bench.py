@@ -225,8 +225,12 @@ def bench_multi(args):
     if args.chunk <= 0:
         whole = 28 * 256 * 8
         ncu = torch.cuda.get_device_properties(0).multi_processor_count
-        per_cu = -(-L // ncu)
-        args.chunk = whole if L >= 2 * whole * ncu else -(-per_cu // 2048) * 2048
+        # one chunk per CU for a single-piece shard; four for shards of several
+        # pieces, whose chunks end unevenly at the piece boundaries
+        npieces = len(z.zs_plan_chunks(numel, wl.p, k, whole)[0])
+        split = ncu if npieces == 1 else 4 * ncu
+        per = -(-L // split)
+        args.chunk = whole if L >= 2 * whole * ncu else -(-per // 2048) * 2048
     pieces, nchunks = z.zs_plan_chunks(numel, wl.p, k, args.chunk)
     print(f"[bench] {wl.name}: N={wl.n} P={wl.p} k={k} L={L} pieces={len(pieces)} "
           f"chunks={nchunks} chunk_elems={args.chunk}", file=sys.stderr, flush=True)
@@ -450,7 +454,8 @@ def main():
     ap.add_argument("--chunk", type=int, default=0,
                     help="chunk-table chunk length in elements (multi-tensor workloads); 0 picks "
                          "one whole kernel chunk (57,344), or for shards under two of those per "
-                         "CU, the shard split evenly over the CUs (rounded up to 2,048)")
+                         "CU, the shard's per-CU share (a quarter of it when the shard spans "
+                         "several tensors), rounded up to 2,048")
     ap.add_argument("--shard", type=int, default=None,
                     help="chunk-table workloads: the rank k whose shard is timed")
     ap.add_argument("--bucket-elems", type=int, default=0,

@@ -176,7 +176,9 @@ zs_status zs_adam_step(const float* g, float* w, float* m, float* v, void* param
  * workgroup per CU takes one chunk at a time, so the chunk is the unit of
  * load balance.  A good chunk_elems is 57,344 (= 28 * 256 * 8, the kernel's
  * whole chunk).  For a shard under two of those per CU, use the shard
- * length divided by the CU count, rounded up to a multiple of 2,048. */
+ * length divided by the CU count, rounded up to a multiple of 2,048, and a
+ * quarter of that when the shard has several pieces (more chunks per CU even
+ * things out where the pieces end). */
 typedef struct {
   int32_t tensor;      /* index in the caller's tensor list */
   int32_t reserved;
