@@ -451,6 +451,8 @@ def main():
     ap.add_argument("--form", default=None,
                     choices=["standard", "page1_literal", "sgd", "sgd_momentum"],
                     help="override the workload's update form (bytes per element follow it)")
+    ap.add_argument("--dtype", default=None, choices=["f16", "bf16"],
+                    help="override the workload's gradient and working-copy dtype")
     ap.add_argument("--chunk", type=int, default=0,
                     help="chunk-table chunk length in elements (multi-tensor workloads); 0 picks "
                          "one whole kernel chunk (57,344), or for shards under two of those per "
@@ -483,10 +485,13 @@ def main():
     if args.workload not in WORKLOADS:
         print(f"unknown workload {args.workload}; one of {sorted(WORKLOADS)}", file=sys.stderr)
         sys.exit(2)
-    if args.form is not None:
+    if args.form is not None or args.dtype is not None:
         import dataclasses
 
-        WORKLOADS[args.workload] = dataclasses.replace(WORKLOADS[args.workload], form=args.form)
+        wl = WORKLOADS[args.workload]
+        WORKLOADS[args.workload] = dataclasses.replace(
+            wl, form=args.form or wl.form, grad_dtype=args.dtype or wl.grad_dtype,
+            param_dtype=args.dtype or wl.param_dtype)
     if args.cpu_offload:
         z.lib()  # fails loudly if the library is not built
         bench_cpu_offload(args)
@@ -512,7 +517,8 @@ def main():
     launch_ms = ms / r["launches"]
     alg_bytes = r["bytes_per_elem"] * r["launch_elems"]
     gbs = alg_bytes / (launch_ms / 1e3) / 1e9
-    traffic = measured_traffic(wl.name, wl.form)
+    # the stored counters were taken at the workload's own dtypes
+    traffic = measured_traffic(wl.name, wl.form) if args.dtype is None else None
     out = {
         "metric": METRIC,
         "value": elems_per_s,

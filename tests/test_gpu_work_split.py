@@ -4,7 +4,9 @@ element checked against the oracle.
 The kernel runs whole chunks (28 vectors of 8 elements per lane, 57,344
 elements per block) in balanced rounds over its blocks (one per CU), keeps a
 last partial round only when it fills at least half of the blocks, and
-deals the rest out as two-vector pieces.  The shard lengths below are chosen
+deals the rest out as two-vector pieces.  A shard under half a whole chunk
+per CU goes to the small-shard kernel instead (pieces only, four workgroups
+per CU).  The shard lengths below are chosen
 from the device's CU count to land in each regime: a last round under half
 full (whole rounds + pieces), one over half full (whole chunks only, plus a
 short tail), a shard smaller than one round (pieces only), and lengths that
@@ -80,3 +82,13 @@ def test_work_split_heads_and_tails(tail, offset):
     cu = _cu()
     L = (cu // 2) * CHUNK + 8 * 511 + tail
     _run(L, 3, "bf16", 1, seed_for(61, tail, offset), offset=offset)
+
+
+@pytest.mark.parametrize("p", [1, 5, 19])
+def test_small_shard_kernel(p):
+    # just under half a whole chunk per CU: the small-shard kernel (four
+    # workgroups per CU, ranks in batches of at most 8: 19 = 8 + 8 + 2 + 1)
+    cu = _cu()
+    L = (cu // 2 - 1) * CHUNK + 8 * 77 + 3
+    say(f"small-shard kernel: L={L}, p={p} on {cu} CUs")
+    _run(L, p, "bf16", 2, seed_for(62, p), offset=p % 4)
