@@ -131,9 +131,9 @@ def _bytes_per_elem(wl):
     return 2 * wl.p + z.BYTES_PER_ELEM[z.FORMS[wl.form]]
 
 
-def bench_single(args):
-    """Fused single-tensor step on one shard with P separate gradient slices."""
-    import numpy as np
+def _single_setup(args):
+    """Inputs of one shard of a single-tensor workload, resident in HBM: P
+    separate gradient slices, the fp32 state and the working copy."""
     import torch
 
     from adam_zs_shard_amd import zshard as z
@@ -157,36 +157,72 @@ def bench_single(args):
     else:
         param = torch.empty(L, dtype=td[wl.param_dtype], device=dev)
         pbase = s[k]
-    gbase = s[k] if wl.grad_layout == "slice" else 0
     assert wl.grad_layout == "slice"
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
+    return dict(wl=wl, k=k, L=L, s=s, grads=grads, w=w, m=m, v=v, param=param, pbase=pbase,
+                gbase=s[k], stream=torch.cuda.current_stream())
+
+
+def bench_single(args):
+    """Fused single-tensor step on one shard with P separate gradient slices."""
+    from adam_zs_shard_amd import zshard as z
+
+    x = _single_setup(args)
+    wl, k, L = x["wl"], x["k"], x["L"]
+    grads, w, m, v, param, stream = x["grads"], x["w"], x["m"], x["v"], x["param"], x["stream"]
 
     def step(i):
         z.zs_fused_shard_step(wl.n, wl.p, k, grads, w, m, v, param,
                               z.hparams(wl.lr, wl.beta1, wl.beta2, wl.eps, i + 1, wl.form),
-                              grad_base=gbase, param_base=pbase, stream=stream.cuda_stream)
+                              grad_base=x["gbase"], param_base=x["pbase"],
+                              stream=stream.cuda_stream)
 
     ms, wall = _time_steps(step, args.steps, args.warmup, stream)
-    bytes_per_elem = _bytes_per_elem(wl)
-    launches_per_step = 1
-    elems = L
+    cpu = None if args.no_cpu_baseline else _cpu_leg(args, wl, grads, w, m, v, f"shard {k}")
+    return dict(wl=wl, k=k, elems=L, ms=ms, wall=wall, bytes_per_elem=_bytes_per_elem(wl),
+                launches=1, launch_elems=L, cpu=cpu)
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        S = min(L, args.cpu_sample)
-        a0 = (L - S) // 2
-        gh = [g[a0:a0 + S].view(torch.int16).cpu().numpy().view(np.uint16) for g in grads]
-        wh = w[a0:a0 + S].cpu().numpy().copy()
-        mh = m[a0:a0 + S].cpu().numpy().copy() if m is not None else np.zeros(S, np.float32)
-        vh = v[a0:a0 + S].cpu().numpy().copy() if v is not None else np.zeros(S, np.float32)
-        thr = host_threads()
-        secs = cpu_baseline(wl.grad_dtype, wl.param_dtype, gh, wh, mh, vh, thr, wl.form)
-        cpu = {"value": S / secs, "unit": "elements/s", "cores": thr, "kind": "oracle",
-               "sample": f"{S} contiguous elements from the middle of shard {k} "
-                         f"({wl.p} ranks), one step, {secs:.2f} s wall on {thr} threads"}
-    return dict(wl=wl, k=k, elems=elems, ms=ms, wall=wall, bytes_per_elem=bytes_per_elem,
-                launches=launches_per_step, launch_elems=L, cpu=cpu)
+
+def bench_unfused(args):
+    """The unfused pair on the same shard: zs_reduce_scatter_mean_local stores
+    the fp32 rank-order mean (2P + 4 B/element), then zs_adam_step reads it
+    (the form's bytes + 4).  Each kernel is also timed alone; the roofline
+    entry is the mean kernel's, which moves most of the bytes."""
+    import torch
+
+    from adam_zs_shard_amd import zshard as z
+
+    x = _single_setup(args)
+    wl, k, L = x["wl"], x["k"], x["L"]
+    grads, w, m, v, param, stream = x["grads"], x["w"], x["m"], x["v"], x["param"], x["stream"]
+    gmean = torch.empty(L, dtype=torch.float32, device="cuda")
+    pslice = param.narrow(0, x["s"][k], L) if wl.param_layout == "full" else param
+    st = stream.cuda_stream
+
+    def mean(i):
+        z.zs_reduce_scatter_mean_local(grads, wl.n, wl.p, k, gmean, grad_base=x["gbase"],
+                                       stream=st)
+
+    def adam(i):
+        z.zs_adam_step(gmean, w, m, v, pslice, L,
+                       z.hparams(wl.lr, wl.beta1, wl.beta2, wl.eps, i + 1, wl.form), stream=st)
+
+    def pair(i):
+        mean(i)
+        adam(i)
+
+    ms, wall = _time_steps(pair, args.steps, args.warmup, stream)
+    ms_mean, _ = _time_steps(mean, args.steps, args.warmup, stream)
+    ms_adam, _ = _time_steps(adam, args.steps, args.warmup, stream)
+    b_mean = 2 * wl.p + 4
+    b_adam = z.BYTES_PER_ELEM[z.FORMS[wl.form]] + 4
+    cpu = None if args.no_cpu_baseline else _cpu_leg(args, wl, grads, w, m, v, f"shard {k}")
+    return dict(wl=wl, k=k, elems=L, ms=ms, wall=wall, bytes_per_elem=b_mean + b_adam,
+                launches=2, launch_elems=L, cpu=cpu,
+                dominant=dict(name="mean_kernel", ms=ms_mean, bytes_per_elem=b_mean),
+                extra={"path": "unfused (zs_reduce_scatter_mean_local + zs_adam_step)",
+                       "mean_kernel_ms": ms_mean, "adam_kernel_ms": ms_adam,
+                       "adam_kernel_gbs": b_adam * L / (ms_adam / 1e3) / 1e9})
 
 
 def _cpu_leg(args, wl, grads, w, m, v, label):
@@ -453,6 +489,9 @@ def main():
                     help="override the workload's update form (bytes per element follow it)")
     ap.add_argument("--dtype", default=None, choices=["f16", "bf16"],
                     help="override the workload's gradient and working-copy dtype")
+    ap.add_argument("--unfused", action="store_true",
+                    help="single-tensor workloads: time the unfused pair (stored fp32 mean, "
+                         "then the separate update) instead of the fused step")
     ap.add_argument("--chunk", type=int, default=0,
                     help="chunk-table chunk length in elements (multi-tensor workloads); 0 picks "
                          "one whole kernel chunk (57,344), or for shards under two of those per "
@@ -505,7 +544,13 @@ def main():
 
     z.lib()  # fails loudly if the HIP library is not built
     wlx = WORKLOADS[args.workload]
-    if wlx.param_layout == "tensors":
+    if args.unfused:
+        if wlx.param_layout == "tensors" or wlx.grad_layout != "slice":
+            print("--unfused times single-tensor workloads with slice gradients",
+                  file=sys.stderr)
+            sys.exit(2)
+        r = bench_unfused(args)
+    elif wlx.param_layout == "tensors":
         r = bench_multi(args)
     elif wlx.grad_layout == "full":
         r = bench_all_shards(args)
@@ -514,11 +559,20 @@ def main():
     wl = r["wl"]
     ms = r["ms"]
     elems_per_s = r["elems"] / (ms / 1e3)
-    launch_ms = ms / r["launches"]
-    alg_bytes = r["bytes_per_elem"] * r["launch_elems"]
-    gbs = alg_bytes / (launch_ms / 1e3) / 1e9
-    # the stored counters were taken at the workload's own dtypes
-    traffic = measured_traffic(wl.name, wl.form) if args.dtype is None else None
+    dom = r.get("dominant")
+    if dom is None:  # every launch of the step is the same kernel on equal work
+        launch_ms = ms / r["launches"]
+        alg_bytes = r["bytes_per_elem"] * r["launch_elems"]
+        gbs = alg_bytes / (launch_ms / 1e3) / 1e9
+        k_gbs = gbs
+        # the stored counters were taken at the workload's own dtypes
+        traffic = measured_traffic(wl.name, wl.form) if args.dtype is None else None
+    else:  # different kernels: the step's rate, and the dominant kernel's roofline
+        gbs = r["bytes_per_elem"] * r["elems"] / (ms / 1e3) / 1e9
+        launch_ms = dom["ms"]
+        alg_bytes = dom["bytes_per_elem"] * r["launch_elems"]
+        k_gbs = alg_bytes / (launch_ms / 1e3) / 1e9
+        traffic = None
     out = {
         "metric": METRIC,
         "value": elems_per_s,
@@ -539,10 +593,11 @@ def main():
                        **r.get("extra", {})),
         "hbm_gbs": gbs,
         "pct_hbm_peak": 100.0 * gbs / HBM_PEAK_GBS,
-        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": traffic,
+        "roofline": {"bound": "hbm", "achieved": k_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": k_gbs / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": alg_bytes,
-                     "bytes_per_element": r["bytes_per_elem"], "kernel_ms": launch_ms},
+                     "bytes_per_element": dom["bytes_per_elem"] if dom else r["bytes_per_elem"],
+                     "kernel_ms": launch_ms},
         "cpu_baseline": r["cpu"],
         "wall_s_timed": r["wall"],
     }

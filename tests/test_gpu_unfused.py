@@ -1,5 +1,7 @@
 """GPU parity of the unfused pair: zs_reduce_scatter_mean_local (fp32 mean,
-bit-exact) and zs_adam_step, and their composition against the fused step."""
+bit-exact; small shards by a grid-stride kernel, shards with whole chunks
+for at least half the CUs by the chunked kernel) and zs_adam_step, and their
+composition against the fused step."""
 
 import numpy as np
 import pytest
@@ -94,3 +96,47 @@ def test_unfused_pair_equals_fused(gdt):
     for x, y in zip(a, b):
         assert torch.equal(x.view(torch.int32), y.view(torch.int32))
     assert torch.equal(pa[s[k]:e[k]].view(torch.int16), pb.view(torch.int16))
+
+
+@pytest.mark.parametrize("p,dt,regime", [(3, "f16", "rounds_plus_pieces"),
+                                         (32, "bf16", "half_round"),
+                                         (17, "f16", "all_whole")])
+def test_mean_whole_chunk_path(p, dt, regime):
+    # shards with whole chunks for at least half the CUs take the chunked mean
+    # kernel (one workgroup per CU, the fused kernel's read phase); shard 1
+    # starts at an element that is not a multiple of 8, so a head is peeled
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    chunk = 28 * 256 * 8
+    chunks = {"rounds_plus_pieces": cu + cu // 4, "half_round": cu // 2,
+              "all_whole": cu + (3 * cu) // 4}[regime]
+    L = chunks * chunk + 8 * 333 + 5
+    n, k = L * p, 1
+    M, s, e = oracle.plan_shards(n, p)
+    assert e[k] - s[k] == L and s[k] % 8 != 0
+    gb = [_bits(L, dt, 1e-2, seed_for(37, p, r)) for r in range(p)]
+    gd = [to_dev_u16(b, TD[dt]) for b in gb]
+    out = torch.full((L + 16,), float("nan"), device=DEV)
+    z.zs_reduce_scatter_mean_local(gd, n, p, k, out[:L], grad_base=s[k])
+    torch.cuda.synchronize()
+    want = oracle.grad_mean(dt, gb)
+    got = f32(out)
+    assert np.array_equal(got[:L].view(np.uint32), want.view(np.uint32))
+    assert np.isnan(got[L:]).all(), "write past the shard"
+
+
+@pytest.mark.parametrize("L", [7, 4096, 4096 * 3 + 8 * 5 + 3, 1_000_003])
+def test_adam_step_pairs_and_tails(L):
+    # the Adam kernel takes two vectors per lane; lengths around that pairing
+    g = normal(L, 1e-2, seed_for(38, L)).numpy()
+    w0 = normal(L, 0.02, seed_for(39, L)).numpy()
+    m0, v0 = (x.numpy() for x in make.random_state(L, 40))
+    gd, wd, md, vd = (torch.from_numpy(x.copy()).to(DEV) for x in (g, w0, m0, v0))
+    pbuf = torch.zeros(L + 8, dtype=torch.float16, device=DEV)
+    z.zs_adam_step(gd, wd, md, vd, pbuf[:L], L, z.hparams(LR, B1, B2, EPS, 2))
+    torch.cuda.synchronize()
+    wh, mh, vh = w0.copy(), m0.copy(), v0.copy()
+    ph = oracle.adam_apply(g, wh, mh, vh, "f16", LR, B1, B2, EPS, 2)
+    assert check_f32(f32(wd), wh, 2e-6, "w") + check_f32(f32(md), mh, 2e-6, "m") == 0
+    assert check_f32(f32(vd), vh, 2e-6, "v") == 0
+    assert check_param(u16(pbuf[:L]), ph, "f16", "param") == 0
+    assert not u16(pbuf[L:]).any(), "write past the shard"
