@@ -1007,6 +1007,58 @@ __global__ __launch_bounds__(kBlock) void adam_kernel(const float* __restrict__ 
   }
 }
 
+// The update from a stored gradient (the unfused second half) for shards
+// with whole chunks for at least half the CUs, in the shape of fused_kernel's
+// update phase: whole chunks round-robin over one workgroup per CU (one wave
+// per SIMD), the chunk's groups one after another.  16% faster than
+// adam_kernel on the 117M-element shard.
+template <int PDT, int FORM, bool PARAM>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void adam_chunk_kernel(const float* __restrict__ gin, float* __restrict__ w,
+                       float* __restrict__ m, float* __restrict__ v,
+                       uint16_t* __restrict__ par, int64_t len, int head, Consts c) {
+  const int tid = threadIdx.x;
+  const uint32_t lane16 = static_cast<uint32_t>(tid) * 16u;
+  const uint32_t lane32 = static_cast<uint32_t>(tid) * 32u;
+  const int64_t h = head < len ? head : len;
+  const int64_t nvec = (len - h) / kVec;
+  constexpr int64_t kFull = static_cast<int64_t>(kBlock) * kGroupsMax;
+  const int64_t nfull = nvec / kFull;
+  for (int64_t ch = blockIdx.x; ch < nfull; ch += gridDim.x) {
+    const int64_t g0 = ch * kFull;
+#pragma unroll
+    for (int u = 0; u < kGroupsMax; ++u) {
+      const int64_t e0 = h + (g0 + static_cast<int64_t>(u) * kBlock) * kVec;
+      const f32x4 a = ld_f32x4(gin + e0, lane32), b = ld_f32x4(gin + e0, lane32 + 16);
+      const float g[kVec] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      adam8<PDT, FORM, PARAM>(c, g, w, m, v, par, e0, lane16, lane32);
+    }
+  }
+  // the vectors after the whole chunks (fewer than one chunk), grid-stride
+  for (int64_t gb = nfull * kFull + static_cast<int64_t>(blockIdx.x) * kBlock; gb < nvec;
+       gb += static_cast<int64_t>(gridDim.x) * kBlock) {
+    if (gb + tid < nvec) {
+      const int64_t e0 = h + gb * kVec;
+      const f32x4 a = ld_f32x4(gin + e0, lane32), b = ld_f32x4(gin + e0, lane32 + 16);
+      const float g[kVec] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      adam8<PDT, FORM, PARAM>(c, g, w, m, v, par, e0, lane16, lane32);
+    }
+  }
+  if (blockIdx.x == 0) {
+    const int64_t t0 = h + nvec * kVec;
+    const int64_t nsc = h + (len - t0);
+    for (int64_t i = tid; i < nsc; i += kBlock) {
+      const int64_t e = i < h ? i : t0 + (i - h);
+      float W = w[e], M = ld_state1<kUsesM<FORM>>(m + e), V = ld_state1<kUsesV<FORM>>(v + e);
+      adam1<FORM>(c, gin[e], W, M, V);
+      w[e] = W;
+      st_state1<kUsesM<FORM>>(m + e, M);
+      st_state1<kUsesV<FORM>>(v + e, V);
+      if constexpr (PARAM) par[e] = narrow1<PDT>(W);
+    }
+  }
+}
+
 constexpr int kBlocksPerCU = 4;
 
 int64_t grid_for(int64_t len) {
@@ -1130,17 +1182,30 @@ hipError_t launch_mean(const MeanLaunch& a) {
 }
 
 hipError_t launch_adam(const AdamLaunch& a) {
-  const int64_t grid = grid_for(a.len);
+  // Shards with whole chunks for at least half the CUs: adam_chunk_kernel,
+  // one workgroup per CU; smaller ones: the grid-stride adam_kernel.
+  const int64_t h = a.head < a.len ? a.head : a.len;
+  const int64_t nvec = (a.len - h) / kVec;
+  const int64_t cu = cu_count();
+  constexpr int64_t kFull = static_cast<int64_t>(kBlock) * kGroupsMax;
+  const bool chunked = 2 * (nvec / kFull) >= cu;
+  const int64_t grid = chunked ? cu : grid_for(a.len);
+  const dim3 gd(static_cast<unsigned>(grid)), bd(kBlock);
   with_dt(a.pdt, [&](auto H) {
     with_form(a.form, [&](auto F) {
-      if (a.param)
-        adam_kernel<decltype(H)::value, decltype(F)::value, true>
-            <<<dim3(static_cast<unsigned>(grid)), dim3(kBlock), 0, a.stream>>>(
-                a.g, a.w, a.m, a.v, a.param, a.len, a.head, a.c);
+      constexpr int PDT = decltype(H)::value, FORM = decltype(F)::value;
+      if (chunked && a.param)
+        adam_chunk_kernel<PDT, FORM, true><<<gd, bd, 0, a.stream>>>(
+            a.g, a.w, a.m, a.v, a.param, a.len, a.head, a.c);
+      else if (chunked)
+        adam_chunk_kernel<PDT, FORM, false><<<gd, bd, 0, a.stream>>>(
+            a.g, a.w, a.m, a.v, a.param, a.len, a.head, a.c);
+      else if (a.param)
+        adam_kernel<PDT, FORM, true><<<gd, bd, 0, a.stream>>>(
+            a.g, a.w, a.m, a.v, a.param, a.len, a.head, a.c);
       else
-        adam_kernel<decltype(H)::value, decltype(F)::value, false>
-            <<<dim3(static_cast<unsigned>(grid)), dim3(kBlock), 0, a.stream>>>(
-                a.g, a.w, a.m, a.v, a.param, a.len, a.head, a.c);
+        adam_kernel<PDT, FORM, false><<<gd, bd, 0, a.stream>>>(
+            a.g, a.w, a.m, a.v, a.param, a.len, a.head, a.c);
     });
   });
   return hipGetLastError();

@@ -140,3 +140,38 @@ def test_adam_step_pairs_and_tails(L):
     assert check_f32(f32(vd), vh, 2e-6, "v") == 0
     assert check_param(u16(pbuf[:L]), ph, "f16", "param") == 0
     assert not u16(pbuf[L:]).any(), "write past the shard"
+
+
+@pytest.mark.parametrize("with_param,off", [(True, 3), (False, 0)])
+def test_adam_step_whole_chunk_path(with_param, off):
+    # shards with whole chunks for at least half the CUs take the chunked Adam
+    # kernel; the arrays start `off` elements into their buffers (a head of
+    # scalar elements when the start is not 8-aligned)
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    L = (cu + cu // 4) * 28 * 256 * 8 + 8 * 333 + 5
+    g = normal(L, 1e-2, seed_for(41, off)).numpy()
+    w0 = normal(L, 0.02, seed_for(42, off)).numpy()
+    m0, v0 = (x.numpy() for x in make.random_state(L, 43))
+
+    def dev(x):
+        buf = torch.zeros(L + off, dtype=torch.float32, device=DEV)
+        buf[off:].copy_(torch.from_numpy(x))
+        return buf[off:]
+
+    gd, wd, md, vd = dev(g), dev(w0), dev(m0), dev(v0)
+    pbuf = torch.zeros(L + off + 8, dtype=torch.bfloat16, device=DEV)
+    par = pbuf[off:off + L] if with_param else None
+    for t in (1, 2):
+        z.zs_adam_step(gd, wd, md, vd, par, L, z.hparams(LR, B1, B2, EPS, t, "page1_literal"),
+                       param_dtype=None if with_param else "bf16")
+    torch.cuda.synchronize()
+    wh, mh, vh = w0.copy(), m0.copy(), v0.copy()
+    for t in (1, 2):
+        ph = oracle.adam_apply(g, wh, mh, vh, "bf16", LR, B1, B2, EPS, t, "page1_literal")
+    d = check_f32(f32(wd), wh, 2e-6, "w") + check_f32(f32(md), mh, 2e-6, "m")
+    d += check_f32(f32(vd), vh, 2e-6, "v")
+    if with_param:
+        d += check_param(u16(par), ph, "bf16", "param")
+        canary = u16(pbuf)
+        assert not canary[:off].any() and not canary[off + L:].any(), "write outside the shard"
+    assert d == 0
