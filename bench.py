@@ -524,6 +524,10 @@ def main():
     if args.workload not in WORKLOADS:
         print(f"unknown workload {args.workload}; one of {sorted(WORKLOADS)}", file=sys.stderr)
         sys.exit(2)
+    wl0 = WORKLOADS[args.workload]
+    if args.unfused and (wl0.param_layout == "tensors" or wl0.grad_layout != "slice"):
+        print("--unfused times single-tensor workloads with slice gradients", file=sys.stderr)
+        sys.exit(2)
     if args.form is not None or args.dtype is not None:
         import dataclasses
 
@@ -545,10 +549,6 @@ def main():
     z.lib()  # fails loudly if the HIP library is not built
     wlx = WORKLOADS[args.workload]
     if args.unfused:
-        if wlx.param_layout == "tensors" or wlx.grad_layout != "slice":
-            print("--unfused times single-tensor workloads with slice gradients",
-                  file=sys.stderr)
-            sys.exit(2)
         r = bench_unfused(args)
     elif wlx.param_layout == "tensors":
         r = bench_multi(args)
