@@ -686,8 +686,12 @@ void table_kernel(TableSrc src, int p, Consts c) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    fused_rest<GDT, PDT, FORM>(gr, p, w, m, v, par, R.len, h, nvec, nfull * kFull, nfull, c,
-                               R.blk, R.nblk, lane16, lane32);
+    // fp16 gradients take rank batches of 8 in the pieces: with 16 the
+    // fp16 Adam instances spill 272 bytes; 8 leaves 44 and makes short-chunk
+    // fp16 tables 5% faster (GPT-2 shard 7); bf16 keeps 16.
+    fused_rest<GDT, PDT, FORM, GDT == kF16 ? 8 : 16>(gr, p, w, m, v, par, R.len, h, nvec,
+                                                     nfull * kFull, nfull, c, R.blk, R.nblk,
+                                                     lane16, lane32);
   }
 }
 
