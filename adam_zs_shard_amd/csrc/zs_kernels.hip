@@ -645,16 +645,17 @@ void table_kernel(TableSrc src, int p, Consts c) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      // update phase: mean, Adam, stores, 2 groups at a time (the state loads
-      // of two groups in flight together: 26% faster than one group at a time
-      // on the 8-rank Llama-3-8B shard, 1.4% slower on the 64-rank shard, where
-      // fused_kernel keeps one group at a time)
-      static_assert(kGroupsMax % 2 == 0, "whole update batches per chunk");
+      // update phase: mean, Adam, stores, kUG groups at a time.  One group,
+      // as in fused_kernel: with two groups' state loads in flight the 8-rank
+      // Llama-3-8B shard ran 0.7% slower and wrote 11% more bytes to HBM than
+      // the model (one group: 4.5%).
+      constexpr int kUG = 1;
+      static_assert(kGroupsMax % kUG == 0, "whole update batches per chunk");
 #pragma unroll
-      for (int u0 = 0; u0 < kGroupsMax; u0 += 2) {
-        f32x4 A[2][6];
+      for (int u0 = 0; u0 < kGroupsMax; u0 += kUG) {
+        f32x4 A[kUG][6];
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < kUG; ++q) {
           const int64_t e0 = h + (g0 + static_cast<int64_t>(u0 + q) * kBlock) * kVec;
           A[q][0] = ld_f32x4(w + e0, lane32);
           A[q][1] = ld_f32x4(w + e0, lane32 + 16);
@@ -665,7 +666,7 @@ void table_kernel(TableSrc src, int p, Consts c) {
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < kUG; ++q) {
           const int u = u0 + q;
           const int64_t e0 = h + (g0 + static_cast<int64_t>(u) * kBlock) * kVec;
           float W[kVec] = {A[q][0].x, A[q][0].y, A[q][0].z, A[q][0].w, A[q][1].x, A[q][1].y, A[q][1].z, A[q][1].w};
