@@ -92,3 +92,14 @@ def test_small_shard_kernel(p):
     L = (cu // 2 - 1) * CHUNK + 8 * 77 + 3
     say(f"small-shard kernel: L={L}, p={p} on {cu} CUs")
     _run(L, p, "bf16", 2, seed_for(62, p), offset=p % 4)
+
+
+@pytest.mark.parametrize("p", [65, 128])
+def test_whole_chunks_beyond_64_ranks(p):
+    # more than 64 ranks takes the kernel instance with room for 256 gradient
+    # pointers; a shard with whole chunks for half the CUs and one more runs
+    # its whole-chunk rank loop, then the pieces and a ragged tail
+    cu = _cu()
+    L = (cu // 2 + 1) * CHUNK + 8 * 21 + 3
+    say(f"whole chunks at {p} ranks: L={L} on {cu} CUs")
+    _run(L, p, "f16", 1, seed_for(63, p), offset=1)
