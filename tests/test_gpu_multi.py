@@ -152,3 +152,15 @@ def test_multi_equals_single_tensor_step():
     torch.cuda.synchronize()
     assert torch.equal(w.view(torch.int32), case.w.view(torch.int32))
     assert torch.equal(par.view(torch.int16), case.params[0].view(torch.int16))
+
+
+def test_two_hundred_ranks_with_whole_chunks():
+    # 200 ranks (table entries stage 200 gradient pointers each) and a shard
+    # that crosses a 7-element tensor: whole kernel chunks in the large pieces,
+    # then their remainders and the tiny piece
+    numel = [1_000_003, 35_999_997, 7, 22_999_993]
+    p, k = 200, 123
+    case = MtCase(numel, p, k, "f16", "f16", 28 * 256 * 8, 48)
+    assert [pc[3] for pc in case.pieces] == [100_000, 7, 199_993]
+    say(f"200 ranks: shard {k}, pieces {[pc[3] for pc in case.pieces]}, {case.nchunks} chunks")
+    _run_and_check(case, 2, 49)

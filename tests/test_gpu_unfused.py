@@ -100,7 +100,8 @@ def test_unfused_pair_equals_fused(gdt):
 
 @pytest.mark.parametrize("p,dt,regime", [(3, "f16", "rounds_plus_pieces"),
                                          (32, "bf16", "half_round"),
-                                         (17, "f16", "all_whole")])
+                                         (17, "f16", "all_whole"),
+                                         (100, "bf16", "half_round")])
 def test_mean_whole_chunk_path(p, dt, regime):
     # shards with whole chunks for at least half the CUs take the chunked mean
     # kernel (one workgroup per CU, the fused kernel's read phase); shard 1
