@@ -186,3 +186,25 @@ def test_zero_7p5b_p64_momentum_sampled():
         d += check_param(u16(param[s[k] + idev]), ph, "f16", "param")
         assert d == 0, f"{d} sampled values differ at t={t}"
         say(f"  7.5B momentum step {t}: {idx.size} samples bit-identical")
+
+
+@pytest.mark.parametrize("form", ["sgd", "sgd_momentum"])
+def test_adam_step_entry_point_whole_chunks(form):
+    # a length with whole chunks for at least half the CUs takes the chunked
+    # update kernel; v (and for plain SGD m) passed as NULL
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    L = (cu + cu // 4) * CHUNK + 8 * 333 + 5
+    g = normal(L, 1e-2, seed_for(79)).numpy()
+    w0 = normal(L, 0.02, seed_for(80)).numpy()
+    gd, wd = torch.from_numpy(g.copy()).to(DEV), torch.from_numpy(w0.copy()).to(DEV)
+    md = torch.zeros(L, device=DEV) if form == "sgd_momentum" else None
+    par = torch.empty(L, dtype=torch.bfloat16, device=DEV)
+    wh, mh, vh = w0.copy(), np.zeros(L, np.float32), np.zeros(L, np.float32)
+    for t in (1, 2):
+        z.zs_adam_step(gd, wd, md, None, par, L, z.hparams(LR, B1, B2, EPS, t, form))
+        ph = oracle.adam_apply(g, wh, mh, vh, "bf16", LR, B1, B2, EPS, t, form)
+    torch.cuda.synchronize()
+    d = check_f32(f32(wd), wh, 2e-6, "w") + check_param(u16(par), ph, "bf16", "param")
+    if md is not None:
+        d += check_f32(f32(md), mh, 2e-6, "m")
+    assert d == 0
