@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstddef>
 #include <cstring>
 #include <vector>
 
@@ -13,6 +14,8 @@
 #include "zs_internal.h"
 
 static_assert(ZS_MAX_P == zs::kMaxP, "ZS_MAX_P and the kernel table size must agree");
+static_assert(ZS_KERNARG_P == zs::kKernargP, "ZS_KERNARG_P and the kernel arguments must agree");
+static_assert(sizeof(zs::StepTableDev) <= zs::kStepTableHead, "step table layout");
 
 namespace {
 
@@ -75,22 +78,21 @@ struct Range {
 };
 bool overlap(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
 
-// Elements to peel so that as many bytes per element as possible start each
-// 8-element group on a 16-byte boundary.  16-bit streams weigh 2 bytes each
-// (gradients read, the working copy written); fp32 state arrays weigh 8
-// (read and written).
-int choose_head(const std::vector<uintptr_t>& a16, const std::vector<uintptr_t>& a32) {
-  int best = 0, best_score = -1;
-  for (int h = 0; h < zs::kVec; ++h) {
-    int score = 0;
-    for (uintptr_t a : a16) score += ((a + 2u * h) % 16u == 0) ? 2 : 0;
-    for (uintptr_t a : a32) score += ((a + 4u * h) % 16u == 0) ? 8 : 0;
-    if (score > best_score) {
-      best_score = score;
-      best = h;
-    }
+size_t rank_table_bytes(int32_t p) {
+  if (p <= ZS_KERNARG_P || p > ZS_MAX_P) return 0;
+  return (static_cast<size_t>(p) * sizeof(void*) + 255u) & ~static_cast<size_t>(255u);
+}
+
+// Writes the p rank pointers into a device array, in launches of up to
+// kKernargP pointers each, on the stream.
+hipError_t fill_rank_table(const uint16_t* const* ptrs, int32_t p, void* dst, hipStream_t st) {
+  auto** d = static_cast<const uint16_t**>(dst);
+  for (int32_t r0 = 0; r0 < p; r0 += zs::kKernargP) {
+    const int n = std::min<int32_t>(zs::kKernargP, p - r0);
+    const hipError_t e = zs::launch_rank_table(ptrs + r0, n, d + r0, st);
+    if (e != hipSuccess) return e;
   }
-  return best;
+  return hipSuccess;
 }
 
 }  // namespace
@@ -128,6 +130,8 @@ zs_status zs_plan_shards(int64_t n, int32_t p, int64_t* m_out, int64_t* starts, 
   }
   return ZS_OK;
 }
+
+size_t zs_shard_workspace_bytes(int32_t p) { return rank_table_bytes(p); }
 
 zs_status zs_fused_shard_step(const zs_shard_args* a) {
   if (!a) return ZS_ERR_NULL;
@@ -190,19 +194,40 @@ zs_status zs_fused_shard_step(const zs_shard_args* a) {
       if (overlap(writes[i], rd)) return ZS_ERR_ALIAS;
   }
   a16.push_back(pp);
-  L.head = choose_head(a16, a32);
+  L.head = zs::choose_head(a16, a32);
+  L.rank_table = nullptr;
+  if (a->p > ZS_KERNARG_P) {
+    const size_t need = rank_table_bytes(a->p);
+    const uintptr_t pw_ = reinterpret_cast<uintptr_t>(a->workspace);
+    if (!a->workspace || a->workspace_bytes < need || pw_ % 16u != 0) return ZS_ERR_CAPACITY;
+    const Range wsr{pw_, pw_ + need};
+    for (const Range& wr : writes)
+      if (overlap(wsr, wr)) return ZS_ERR_ALIAS;
+    for (const Range& rd : reads)
+      if (overlap(wsr, rd)) return ZS_ERR_ALIAS;
+    L.rank_table = static_cast<const uint16_t* const*>(a->workspace);
+    const hipError_t e = fill_rank_table(L.grads, a->p, a->workspace, L.stream);
+    if (e != hipSuccess) return hip_fail(e);
+  }
 
   const hipError_t err = zs::launch_fused(L);
   if (err != hipSuccess) return hip_fail(err);
   return ZS_OK;
 }
 
-zs_status zs_reduce_scatter_mean_local(const void* const* grads, int32_t grad_dtype,
-                                       int64_t grad_base, int64_t n, int32_t p, int32_t k,
-                                       float* g_out, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The stored mean, fp32 (odt 0) or rounded to 16 bits, in passes of up to
+// kKernargP ranks; between passes the fp32 sums live in `partial` (g_out
+// itself for an fp32 output).
+zs_status mean_impl(const void* const* grads, int32_t grad_dtype, int64_t grad_base, int64_t n,
+                    int32_t p, int32_t k, void* g_out, int32_t odt, float* partial,
+                    void* stream) {
   if (p < 1 || p > ZS_MAX_P || k < 0 || k >= p || n < 0) return ZS_ERR_ARG;
   if (n > kMaxN) return ZS_ERR_RANGE;
-  if (!dtype_ok(grad_dtype)) return ZS_ERR_DTYPE;
+  if (!dtype_ok(grad_dtype) || (odt != 0 && !dtype_ok(odt))) return ZS_ERR_DTYPE;
   if (!grads) return ZS_ERR_NULL;
   int64_t m, s, e;
   shard_bounds(n, p, k, &m, &s, &e);
@@ -212,28 +237,55 @@ zs_status zs_reduce_scatter_mean_local(const void* const* grads, int32_t grad_dt
   if (!g_out) return ZS_ERR_NULL;
   for (int32_t r = 0; r < p; ++r)
     if (!grads[r]) return ZS_ERR_NULL;
+  const bool passes = p > ZS_KERNARG_P;
+  float* acc_buf = odt == 0 ? static_cast<float*>(g_out) : partial;
+  if (passes && !acc_buf) return ZS_ERR_NULL;
 
-  zs::MeanLaunch L;
-  L.p = p;
-  L.gdt = grad_dtype;
-  L.out = g_out;
-  L.len = len;
-  L.PF = static_cast<float>(static_cast<double>(p));
-  L.stream = static_cast<hipStream_t>(stream);
   const uintptr_t po = reinterpret_cast<uintptr_t>(g_out);
-  const Range wr{po, po + 4u * static_cast<uintptr_t>(len)};
+  const uintptr_t ob = (odt == 0 ? 4u : 2u) * static_cast<uintptr_t>(len);
+  std::vector<Range> writes = {{po, po + ob}};
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(acc_buf);
+  if (passes && odt != 0) {
+    writes.push_back({pa, pa + 4u * static_cast<uintptr_t>(len)});
+    if (overlap(writes[0], writes[1])) return ZS_ERR_ALIAS;
+  }
+  std::vector<const uint16_t*> gp(static_cast<size_t>(p));
   std::vector<uintptr_t> a16;
   for (int32_t r = 0; r < p; ++r) {
-    L.grads[r] = static_cast<const uint16_t*>(grads[r]) + (s - grad_base);
-    const uintptr_t g0 = reinterpret_cast<uintptr_t>(L.grads[r]);
-    if (overlap(wr, Range{g0, g0 + 2u * static_cast<uintptr_t>(len)})) return ZS_ERR_ALIAS;
+    gp[r] = static_cast<const uint16_t*>(grads[r]) + (s - grad_base);
+    const uintptr_t g0 = reinterpret_cast<uintptr_t>(gp[r]);
+    for (const Range& wr : writes)
+      if (overlap(wr, Range{g0, g0 + 2u * static_cast<uintptr_t>(len)})) return ZS_ERR_ALIAS;
     a16.push_back(g0);
   }
-  // the fp32 output is written once per element: weigh it like a 16-bit read x2
-  L.head = choose_head(a16, {po});
-  const hipError_t err = zs::launch_mean(L);
+  // the output is written once per element; an fp32 array weighs like the
+  // state arrays, a 16-bit one like a gradient
+  std::vector<uintptr_t> a32;
+  if (odt == 0) a32.push_back(po); else a16.push_back(po);
+  if (passes && odt != 0) a32.push_back(pa);
+
+  const hipError_t err = zs::mean_range(gp.data(), p, grad_dtype, len, zs::choose_head(a16, a32),
+                                        g_out, odt, acc_buf, static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return hip_fail(err);
   return ZS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+zs_status zs_reduce_scatter_mean_local(const void* const* grads, int32_t grad_dtype,
+                                       int64_t grad_base, int64_t n, int32_t p, int32_t k,
+                                       float* g_out, void* stream) {
+  return mean_impl(grads, grad_dtype, grad_base, n, p, k, g_out, 0, nullptr, stream);
+}
+
+zs_status zs_reduce_scatter_mean_local16(const void* const* grads, int32_t grad_dtype,
+                                         int64_t grad_base, int64_t n, int32_t p, int32_t k,
+                                         void* g_out, int32_t out_dtype, float* partial,
+                                         void* stream) {
+  if (!dtype_ok(out_dtype)) return ZS_ERR_DTYPE;
+  return mean_impl(grads, grad_dtype, grad_base, n, p, k, g_out, out_dtype, partial, stream);
 }
 
 zs_status zs_adam_step(const float* g, float* w, float* m, float* v, void* param,
@@ -280,7 +332,7 @@ zs_status zs_adam_step(const float* g, float* w, float* m, float* v, void* param
   L.stream = static_cast<hipStream_t>(stream);
   std::vector<uintptr_t> a16;
   if (param) a16.push_back(pp);
-  L.head = choose_head(a16, a32);
+  L.head = zs::choose_head(a16, a32);
   const hipError_t err = zs::launch_adam(L);
   if (err != hipSuccess) return hip_fail(err);
   return ZS_OK;
@@ -329,9 +381,83 @@ zs_status zs_plan_chunks(const int64_t* numel, int32_t ntensors, int32_t p, int3
   return count > pieces_cap ? ZS_ERR_CAPACITY : ZS_OK;
 }
 
+int64_t zs_mt_chunk_elems(int64_t shard_len, int32_t npieces, int32_t cu_count) {
+  if (shard_len < 0 || npieces < 1) return 0;
+  const int64_t cu = cu_count > 0 ? cu_count : zs::cu_count();
+  constexpr int64_t whole = static_cast<int64_t>(zs::kBlock) * 28 * zs::kVec;  // 57,344
+  if (shard_len >= 2 * whole * cu) return whole;
+  const int64_t split = npieces == 1 ? cu : 4 * cu;
+  const int64_t per = (shard_len + split - 1) / split;
+  const int64_t c = (per + 2047) / 2048 * 2048;
+  return c < 2048 ? 2048 : c;
+}
+
+zs_status zs_plan_buckets(const zs_piece* pieces, int32_t npieces, int64_t bucket_elems,
+                          int32_t* bucket_of, int32_t* nbuckets) {
+  if (!nbuckets || (npieces > 0 && (!pieces || !bucket_of))) return ZS_ERR_NULL;
+  if (npieces < 0) return ZS_ERR_ARG;
+  for (int32_t i = 0; i < npieces; ++i)
+    if (pieces[i].len < 1) return ZS_ERR_ARG;
+  int32_t b = 0;
+  int64_t size = 0;
+  for (int32_t i = 0; i < npieces; ++i) {
+    bucket_of[i] = b;
+    size += pieces[i].len;
+    if (bucket_elems > 0 && size >= bucket_elems && i + 1 < npieces) {
+      ++b;
+      size = 0;
+    }
+  }
+  *nbuckets = npieces > 0 ? b + 1 : 0;
+  return ZS_OK;
+}
+
 }  // extern "C"
 
 namespace zs {
+
+int32_t hip_status(hipError_t e) { return hip_fail(e); }
+
+// Elements to peel so that as many bytes per element as possible start each
+// 8-element group on a 16-byte boundary.  16-bit streams weigh 2 bytes each
+// (gradients read, the working copy written); fp32 state arrays weigh 8
+// (read and written).
+int choose_head(const std::vector<uintptr_t>& a16, const std::vector<uintptr_t>& a32) {
+  int best = 0, best_score = -1;
+  for (int h = 0; h < zs::kVec; ++h) {
+    int score = 0;
+    for (uintptr_t a : a16) score += ((a + 2u * h) % 16u == 0) ? 2 : 0;
+    for (uintptr_t a : a32) score += ((a + 4u * h) % 16u == 0) ? 8 : 0;
+    if (score > best_score) {
+      best_score = score;
+      best = h;
+    }
+  }
+  return best;
+}
+
+hipError_t mean_range(const uint16_t* const* grads, int32_t p, int32_t gdt, int64_t len, int head,
+                      void* out, int32_t odt, float* acc_buf, hipStream_t stream) {
+  MeanLaunch L;
+  L.gdt = gdt;
+  L.odt = odt;
+  L.len = len;
+  L.head = head;
+  L.PF = static_cast<float>(static_cast<double>(p));
+  L.stream = stream;
+  for (int32_t r0 = 0; r0 < p; r0 += kKernargP) {
+    const int32_t np = std::min<int32_t>(kKernargP, p - r0);
+    for (int32_t r = 0; r < np; ++r) L.grads[r] = grads[r0 + r];
+    L.p = np;
+    L.acc = r0 == 0 ? nullptr : acc_buf;
+    L.last = r0 + np == p;
+    L.out = L.last ? out : static_cast<void*>(acc_buf);
+    const hipError_t err = launch_mean(L);
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
 MtLayout mt_layout(int32_t npieces, int64_t nchunks, int32_t p) {
   auto up = [](size_t x) { return (x + 255u) & ~static_cast<size_t>(255u); };
   MtLayout L;
@@ -430,7 +556,7 @@ zs_status zs_mt_upload(const zs_piece* pieces, const zs_piece_ptrs* ptrs, int32_
     std::vector<uintptr_t> a32 = {reinterpret_cast<uintptr_t>(q.w)};
     if (q.m) a32.push_back(reinterpret_cast<uintptr_t>(q.m));
     if (q.v) a32.push_back(reinterpret_cast<uintptr_t>(q.v));
-    d.head = choose_head(a16, a32);
+    d.head = zs::choose_head(a16, a32);
     for (int64_t st = 0; st < d.len; st += chunk_elems) {
       hp_chunks[c].piece = i;
       hp_chunks[c].reserved = 0;
@@ -455,22 +581,29 @@ zs_status zs_mt_upload(const zs_piece* pieces, const zs_piece_ptrs* ptrs, int32_
   return ZS_OK;
 }
 
-zs_status zs_fused_shard_step_multi(const zs_mt_table* t, const zs_adam_hparams* hp,
-                                    void* stream) {
+}  // extern "C"
+
+namespace {
+
+zs_status check_table(const zs_mt_table* t) {
   if (!t) return ZS_ERR_NULL;
-  if (const zs_status st = check_hparams(hp)) return st;
   if (t->p < 1 || t->p > ZS_MAX_P || t->npieces < 0 || t->nchunks < 0 ||
       t->chunk_elems < zs::kVec || t->chunk_elems % zs::kVec != 0)
     return ZS_ERR_ARG;
   if (!dtype_ok(t->grad_dtype) || !dtype_ok(t->param_dtype)) return ZS_ERR_DTYPE;
+  return ZS_OK;
+}
+
+zs_status launch_table(const zs_mt_table* t, int32_t form, const zs::Consts& c,
+                       const zs::StepTableDev* steps, void* stream) {
   if (t->nchunks == 0) return ZS_OK;
-  if ((needs_m(hp->form) && !(t->state & ZS_STATE_M)) ||
-      (needs_v(hp->form) && !(t->state & ZS_STATE_V)))
+  if ((needs_m(form) && !(t->state & ZS_STATE_M)) || (needs_v(form) && !(t->state & ZS_STATE_V)))
     return ZS_ERR_NULL;
   if (!t->workspace) return ZS_ERR_NULL;
   const zs::MtLayout lay = zs::mt_layout(t->npieces, t->nchunks, t->p);
   const auto* base = static_cast<const unsigned char*>(t->workspace);
   zs::MultiLaunch L;
+  L.steps = steps;
   L.pieces = reinterpret_cast<const zs::MtPiece*>(base + lay.pieces_off);
   L.gptrs = reinterpret_cast<const uint16_t* const*>(base + lay.gptr_off);
   L.chunks = reinterpret_cast<const zs::MtChunk*>(base + lay.chunks_off);
@@ -479,12 +612,107 @@ zs_status zs_fused_shard_step_multi(const zs_mt_table* t, const zs_adam_hparams*
   L.p = t->p;
   L.gdt = t->grad_dtype;
   L.pdt = t->param_dtype;
-  L.form = hp->form;
-  L.c = make_consts(*hp, t->p);
+  L.form = form;
+  L.c = c;
   L.stream = static_cast<hipStream_t>(stream);
   const hipError_t err = zs::launch_multi(L);
   if (err != hipSuccess) return hip_fail(err);
   return ZS_OK;
+}
+
+zs_status check_steps(const zs_step_table* st) {
+  if (!st || !st->dev) return ZS_ERR_NULL;
+  if (st->nsteps < 1 || st->p < 1 || st->p > ZS_MAX_P || st->form < ZS_ADAM_STANDARD ||
+      st->form > ZS_SGD_MOMENTUM)
+    return ZS_ERR_ARG;
+  return ZS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+zs_status zs_fused_shard_step_multi(const zs_mt_table* t, const zs_adam_hparams* hp,
+                                    void* stream) {
+  if (const zs_status st = check_table(t)) return st;
+  if (const zs_status st = check_hparams(hp)) return st;
+  return launch_table(t, hp->form, make_consts(*hp, t->p), nullptr, stream);
+}
+
+size_t zs_step_table_bytes(int32_t nsteps) {
+  if (nsteps < 1) return 0;
+  const size_t b = zs::kStepTableHead + sizeof(zs::Consts) * static_cast<size_t>(nsteps);
+  return (b + 255u) & ~static_cast<size_t>(255u);
+}
+
+zs_status zs_step_table_init(const zs_adam_hparams* hp, int32_t p, int32_t nsteps, void* dev,
+                             size_t bytes, void* stream, zs_step_table* table) {
+  if (!table || !dev) return ZS_ERR_NULL;
+  if (const zs_status st = check_hparams(hp)) return st;
+  if (p < 1 || p > ZS_MAX_P || nsteps < 1) return ZS_ERR_ARG;
+  if (hp->step > INT64_MAX - nsteps) return ZS_ERR_RANGE;
+  const size_t need = zs_step_table_bytes(nsteps);
+  if (reinterpret_cast<uintptr_t>(dev) % 256u != 0 || bytes < need) return ZS_ERR_CAPACITY;
+  std::vector<unsigned char> host(need, 0);
+  auto* t = reinterpret_cast<zs::StepTableDev*>(host.data());
+  t->cursor = 0;
+  t->nsteps = nsteps;
+  t->exhausted = 0;
+  t->form = hp->form;
+  t->p = p;
+  t->reserved = 0;
+  t->first_step = hp->step;
+  auto* cs = reinterpret_cast<zs::Consts*>(host.data() + zs::kStepTableHead);
+  for (int32_t i = 0; i < nsteps; ++i) {
+    zs_adam_hparams h = *hp;
+    h.step = hp->step + i;
+    cs[i] = make_consts(h, p);
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err = hipMemcpyAsync(dev, host.data(), need, hipMemcpyHostToDevice, s);
+  if (err != hipSuccess) return hip_fail(err);
+  err = hipStreamSynchronize(s);
+  if (err != hipSuccess) return hip_fail(err);
+  table->dev = dev;
+  table->first_step = hp->step;
+  table->nsteps = nsteps;
+  table->p = p;
+  table->form = hp->form;
+  table->reserved = 0;
+  return ZS_OK;
+}
+
+zs_status zs_step_table_advance(const zs_step_table* table, void* stream) {
+  if (const zs_status st = check_steps(table)) return st;
+  const hipError_t err = zs::launch_step_advance(static_cast<zs::StepTableDev*>(table->dev),
+                                                 static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return hip_fail(err);
+  return ZS_OK;
+}
+
+zs_status zs_step_table_status(const zs_step_table* table, int64_t* cursor, int32_t* exhausted,
+                               void* stream) {
+  if (const zs_status st = check_steps(table)) return st;
+  unsigned char head[sizeof(zs::StepTableDev)];
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err = hipMemcpyAsync(head, table->dev, sizeof(head), hipMemcpyDeviceToHost, s);
+  if (err != hipSuccess) return hip_fail(err);
+  err = hipStreamSynchronize(s);
+  if (err != hipSuccess) return hip_fail(err);
+  zs::StepTableDev t;
+  std::memcpy(&t, head, sizeof(head));
+  if (cursor) *cursor = t.cursor;
+  if (exhausted) *exhausted = t.exhausted;
+  return ZS_OK;
+}
+
+zs_status zs_fused_shard_step_multi_dev(const zs_mt_table* t, const zs_step_table* steps,
+                                        void* stream) {
+  if (const zs_status st = check_table(t)) return st;
+  if (const zs_status st = check_steps(steps)) return st;
+  if (steps->p != t->p) return ZS_ERR_ARG;
+  return launch_table(t, steps->form, zs::Consts{},
+                      static_cast<const zs::StepTableDev*>(steps->dev), stream);
 }
 
 }  // extern "C"

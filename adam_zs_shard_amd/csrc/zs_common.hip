@@ -1,0 +1,59 @@
+// zs_common.hip -- device queries shared by the launchers.
+
+#include "zs_device.h"
+
+namespace zs {
+namespace {
+
+// Copies the n <= kKernargP rank pointers of this launch's kernel arguments
+// into a device array, one pointer per lane.  The pointers are read through
+// the kernel-argument segment (the by-value table is its first argument).
+__global__ __launch_bounds__(kBlock) void rank_table_kernel(GradArgs<kKernargP> ga, int n,
+                                                            const uint16_t** dst) {
+  (void)ga;
+  const KernargTable t = kernarg_grads().t;
+  const int i = threadIdx.x;
+  if (i < n) dst[i] = t[i];
+}
+
+// One thread: the step table's cursor moves to the next entry.
+__global__ void step_advance_kernel(StepTableDev* st) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) st->cursor = st->cursor + 1;
+}
+
+}  // namespace
+
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  if (dev >= 0 && dev < 64) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0)
+    n = 256;
+  if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+hipError_t launch_rank_table(const uint16_t* const* src, int n, const uint16_t** dst,
+                             hipStream_t stream) {
+  GradArgs<kKernargP> ga;
+  for (int r = 0; r < kKernargP; ++r) ga.g[r] = r < n ? src[r] : nullptr;
+  rank_table_kernel<<<dim3(1), dim3(kBlock), 0, stream>>>(ga, n, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_step_advance(StepTableDev* t, hipStream_t stream) {
+  step_advance_kernel<<<dim3(1), dim3(64), 0, stream>>>(t);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused(const FusedLaunch& a) {
+  return a.gdt == kF16 ? launch_fused_f16(a) : launch_fused_bf16(a);
+}
+
+}  // namespace zs

@@ -6,7 +6,7 @@
 // fp32 master weights and moments kept in host memory, then float2half), and
 // the 16-bit parameters go back.  [ZA] §1.6.2 Optimizer Offload: the CPU side
 // uses multithreading + SIMD so that it is not the bottleneck; in the
-// multi-GPU case each GPU's 1/N shard has its own CPU process (§2.2).
+// multi-GPU case each GPU's 1/N shard has its own CPU process (§2.3 扩展性).
 //
 // The arithmetic is the canonical per-element sequence of the GPU path, on
 // 8 lanes at a time with AVX2 and F16C: exact 16 -> 32-bit widening, every

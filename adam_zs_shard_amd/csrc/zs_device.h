@@ -1,0 +1,612 @@
+// zs_device.h -- device helpers shared by the gfx950 kernels of libzshard.
+//
+// The per-shard step is pure streaming: per element it reads P 16-bit
+// gradients and the fp32 (w, m, v), writes (w, m, v) and one 16-bit working
+// copy, and does O(P) flops.  At about 0.5 flop/byte it sits far below the
+// fp32 vector ridge of the chip: the design goal is HBM bandwidth.
+//  - Each lane owns groups of 8 consecutive elements: one 16-byte load per
+//    gradient rank, two per fp32 state array, one 16-byte store of the
+//    16-bit copy.  Addresses are a workgroup-uniform base (SGPRs) plus a
+//    fixed per-lane byte offset, so a wave64 access is 1 KiB contiguous.
+//  - Gradient reads are rank-major: for each rank in turn a wave issues one
+//    load (group 0), uses it, then the other 27 loads of the chunk back to
+//    back (scheduling barriers stop the compiler from sinking each load next
+//    to its use), then adds them into the per-group sums.  Every element receives the ranks in order 0..P-1: a
+//    left fold, one fp32 rounding per add, exactly the oracle's order.
+//    All loads and stores are non-temporal (each byte is touched once).
+//  - Phase separation: HBM on this part streams reads alone far faster than
+//    reads with any writes mixed in.  A workgroup therefore sums the
+//    gradients of a whole chunk (up to 28 groups per lane, held in registers
+//    with one wave per SIMD) before it touches w, m, v and the working copy,
+//    so reads and writes reach the memory in separate stretches.
+//  - One workgroup per CU.  Full chunks (28 groups per lane) go round-robin;
+//    the remainder (at most one chunk's worth, plus up to 14 scalar
+//    elements) is dealt to the workgroups that got one chunk fewer, and is
+//    read with the ranks batched, so the workgroups finish together.
+//    Shards under half a chunk per CU get no whole chunk: small_kernel deals
+//    their pieces over four workgroups per CU instead.
+//  - No MFMA and no LDS on the single-tensor path (nothing is reused); the
+//    multi-tensor path stages one chunk's descriptors in LDS.
+// Arithmetic (rank-order fp32 mean, Adam moments, bias correction, update,
+// round-to-nearest-even downcast) follows the pages cited in zshard.h:
+// [DP-III] §(一) (Adam), §(四) steps 2-4; [EAI19] 通信原语 All-Reduce (mean);
+// [ZP] 核心原理 and [ZA] §2.2 (fp32 update then the 16-bit working copy).
+// Compiled with -ffp-contract=off and the pragma below: no FMA contraction;
+// division and sqrt are the correctly rounded HIP defaults; fp32 denormals
+// are kept.
+
+
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <type_traits>
+
+#include "zs_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace zs {
+namespace {
+
+// 16-byte vectors that may sit at any 2-byte (u16) or 4-byte (fp32) address:
+// gfx950 runs with unaligned access enabled, so these still compile to
+// global_load_dwordx4 / global_store_dwordx4.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4), aligned(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4), aligned(4)));
+
+// Groups of 8 elements per lane whose rank sums are held in registers across
+// the read-only phase of a full chunk (28 x 8 fp32 values per lane: with one
+// wave per SIMD the kernel may use the whole 512-entry register file), the
+// gradient loads a wave issues back to back, and the groups of the smaller
+// chunks that take the remainder of a range.
+constexpr int kGroupsMax = 28;
+// Gradient loads per batch of a rank in the whole-chunk read phase (after
+// the probe load of group 0): fused_kernel issues the rest of the chunk, 27
+// loads, in one batch (1.7% faster at 64 ranks than two batches of 14);
+// table_kernel keeps batches of 14 (0.5% faster at 8 ranks).
+constexpr int kLoadBatch = 28;
+constexpr int kTableLoadBatch = 14;
+static_assert(kGroupsMax % kLoadBatch == 0, "whole load batches per chunk");
+static_assert(kGroupsMax % kTableLoadBatch == 0, "whole load batches per chunk");
+
+template <int DT>
+__device__ __forceinline__ float widen_lo(uint32_t x) {
+  if constexpr (DT == kF16) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(x & 0xffffu)));
+  } else {
+    return __builtin_bit_cast(float, x << 16);
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ float widen_hi(uint32_t x) {
+  if constexpr (DT == kF16) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(x >> 16)));
+  } else {
+    return __builtin_bit_cast(float, x & 0xffff0000u);
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ float widen1(uint16_t h) {
+  return widen_lo<DT>(static_cast<uint32_t>(h));
+}
+
+// fp32 -> 16 bits, round to nearest even (v_cvt_f16_f32 under the default
+// rounding mode; v_cvt_pk_bf16_f32 on gfx950).
+template <int DT>
+__device__ __forceinline__ uint16_t narrow1(float x) {
+  if constexpr (DT == kF16) {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+  } else {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t narrow2(float lo, float hi) {
+  return static_cast<uint32_t>(narrow1<DT>(lo)) | (static_cast<uint32_t>(narrow1<DT>(hi)) << 16);
+}
+
+// One update of one element, in place.  Adam (both forms): the two moment
+// products rounded, their sum rounded; bias correction by division;
+// d = sqrt(v_hat) + eps; u = m_hat / d; w - lr*u.  The SGD forms touch only
+// what they use: w - lr*g, or m = beta1*m + g then w - lr*m.
+template <int FORM>
+__device__ __forceinline__ void adam1(const Consts& c, float g, float& w, float& m, float& v) {
+  if constexpr (FORM == kSgd) {  // w - lr*g; m, v unused
+    w = w - c.LR * g;
+    return;
+  } else if constexpr (FORM == kSgdMomentum) {  // heavy-ball: m = beta1*m + g; w - lr*m
+    m = c.B1 * m + g;
+    w = w - c.LR * m;
+    return;
+  }
+  const float mm = c.B1 * m + c.C1 * g;
+  const float vv = c.B2 * v + c.C2 * (g * g);
+  float mh, vh;
+  if constexpr (FORM == kStandard) {
+    m = mm;
+    v = vv;
+    mh = mm / c.BC1;
+    vh = vv / c.BC2;
+  } else {
+    m = mm / c.BC1;
+    v = vv / c.BC2;
+    mh = m;
+    vh = v;
+  }
+  const float d = __builtin_sqrtf(vh) + c.EPS;
+  const float u = mh / d;
+  w = w - c.LR * u;
+}
+
+template <class T>
+__device__ __forceinline__ T* uniform_t(T* p) {
+  const uint64_t x = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x >> 32));
+  // Rebuilt as a global-memory pointer: a pointer that comes out of LDS is
+  // otherwise generic, and generic (flat) accesses make every wait a full
+  // drain (flat loads may return out of order), which serialises the loads.
+  using GT = __attribute__((address_space(1))) T;
+  return (T*)reinterpret_cast<GT*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+__device__ __forceinline__ const uint16_t* uniform(const uint16_t* p) { return uniform_t(p); }
+
+// Gradient pointer sources: kernel arguments, or a table staged in LDS.  The
+// pointer of a rank is the same for the whole workgroup (uniform).
+template <int PMAX>
+struct GradArgs {
+  const uint16_t* g[PMAX];
+};
+
+// The pointer table is the kernel's first argument, so it sits at offset 0 of
+// the kernel-argument segment; reading it there (scalar loads from the
+// constant address space) avoids any private copy of the by-value table.
+typedef const uint16_t* const __attribute__((address_space(4)))* KernargTable;
+
+struct ArgGrads {
+  KernargTable t;
+  __device__ __forceinline__ const uint16_t* get(int r) const { return t[r]; }
+};
+
+__device__ __forceinline__ ArgGrads kernarg_grads() {
+  return ArgGrads{(KernargTable)(__builtin_amdgcn_kernarg_segment_ptr())};
+}
+
+// The rank pointers from a device array when the launch has one (more ranks
+// than fit in the kernel arguments), else from the kernel arguments.  Both
+// are read-only for the whole launch, so both are read with scalar loads.
+__device__ __forceinline__ ArgGrads rank_grads(const void* table) {
+  return table ? ArgGrads{reinterpret_cast<KernargTable>(reinterpret_cast<uintptr_t>(table))}
+               : kernarg_grads();
+}
+
+struct LdsGrads {
+  const uint16_t* const* s;
+  __device__ __forceinline__ const uint16_t* get(int r) const { return uniform(s[r]); }
+};
+
+constexpr int kRankBatch = 8;
+// Waves per SIMD (workgroups per CU) of the small-shard kernel.
+constexpr int kSmallWaves = 4;
+
+// 16-byte loads at a workgroup-uniform base plus a per-lane byte offset; the
+// gradient loads are non-temporal (each byte is read once per step).
+__device__ __forceinline__ u32x4 ld_grad(const uint16_t* base, uint32_t off) {
+  return __builtin_nontemporal_load(
+      reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + off));
+}
+__device__ __forceinline__ f32x4 ld_f32x4(const float* base, uint32_t off) {
+  return __builtin_nontemporal_load(
+      reinterpret_cast<const f32x4*>(reinterpret_cast<const char*>(base) + off));
+}
+// The fp32 state loads and all stores are non-temporal too: each byte of w,
+// m, v and the working copy is read once and written once per step.  Against
+// plain loads and stores this is about 1.4% faster on the 7.5B-parameter,
+// 64-rank shard; plain gradient loads instead of non-temporal ones cost 10%.
+__device__ __forceinline__ void st_f32x4(float* base, uint32_t off, f32x4 x) {
+  __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(reinterpret_cast<char*>(base) + off));
+}
+__device__ __forceinline__ void st_u16x8(uint16_t* base, uint32_t off, u32x4 x) {
+  __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(reinterpret_cast<char*>(base) + off));
+}
+
+// Which optimizer state a form reads and writes: Adam both moments, momentum
+// SGD the momentum only, plain SGD neither (those pointers may be null).
+template <int FORM>
+constexpr bool kUsesM = FORM != kSgd;
+template <int FORM>
+constexpr bool kUsesV = FORM == kStandard || FORM == kPage1Literal;
+
+template <bool USE>
+__device__ __forceinline__ f32x4 ld_state(const float* base, uint32_t off) {
+  if constexpr (USE) {
+    return ld_f32x4(base, off);
+  } else {
+    return f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+}
+template <bool USE>
+__device__ __forceinline__ void st_state(float* base, uint32_t off, f32x4 x) {
+  if constexpr (USE) st_f32x4(base, off, x);
+}
+template <bool USE>
+__device__ __forceinline__ float ld_state1(const float* p) {
+  if constexpr (USE) {
+    return *p;
+  } else {
+    return 0.0f;
+  }
+}
+template <bool USE>
+__device__ __forceinline__ void st_state1(float* p, float x) {
+  if constexpr (USE) *p = x;
+}
+
+template <int GDT>
+__device__ __forceinline__ void fold8(float (&acc)[kVec], const u32x4& q) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    acc[2 * j] = acc[2 * j] + widen_lo<GDT>(q[j]);
+    acc[2 * j + 1] = acc[2 * j + 1] + widen_hi<GDT>(q[j]);
+  }
+}
+
+template <int GDT>
+__device__ __forceinline__ void init8(float (&acc)[kVec], const u32x4& q) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    acc[2 * j] = widen_lo<GDT>(q[j]);
+    acc[2 * j + 1] = widen_hi<GDT>(q[j]);
+  }
+}
+
+// The loads of ranks r0 .. r0+B-1 for one lane's 8 elements, issued together
+// (the scheduling barriers keep the compiler from sinking each load next to
+// its use, which would leave one load in flight), then added in rank order.
+// CONT: acc already holds the fp32 sums of earlier ranks, so rank r0 = 0 of
+// this call is added to it rather than starting the fold.
+template <int B, int GDT, bool CONT = false, class Grads>
+__device__ __forceinline__ void fold_batch(const Grads& gr, int r0, int64_t e0, uint32_t lane16,
+                                           float (&acc)[kVec]) {
+  u32x4 q[B];
+#pragma unroll
+  for (int b = 0; b < B; ++b) q[b] = ld_grad(gr.get(r0 + b) + e0, lane16);
+  __builtin_amdgcn_sched_barrier(0);
+  if (!CONT && r0 == 0) {
+    init8<GDT>(acc, q[0]);
+  } else {
+    fold8<GDT>(acc, q[0]);
+  }
+#pragma unroll
+  for (int b = 1; b < B; ++b) fold8<GDT>(acc, q[b]);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// acc[j] = sum over ranks r = 0..p-1, in that order, of widen(grad_r[e0 + 8*lane + j]),
+// in batches of 16 ranks, then one batch each of 8, 4, 2, 1 for the rest: at
+// most 4 + P/16 memory round trips.  e0 is workgroup-uniform, lane16 = 16 * lane.
+template <int GDT, bool CONT = false, class Grads>
+__device__ __forceinline__ void sum_ranks8(const Grads& gr, int p, int64_t e0, uint32_t lane16,
+                                           float (&acc)[kVec]) {
+  int r0 = 0;
+  for (; r0 + 16 <= p; r0 += 16) fold_batch<16, GDT, CONT>(gr, r0, e0, lane16, acc);
+  if (r0 + 8 <= p) {
+    fold_batch<8, GDT, CONT>(gr, r0, e0, lane16, acc);
+    r0 += 8;
+  }
+  if (r0 + 4 <= p) {
+    fold_batch<4, GDT, CONT>(gr, r0, e0, lane16, acc);
+    r0 += 4;
+  }
+  if (r0 + 2 <= p) {
+    fold_batch<2, GDT, CONT>(gr, r0, e0, lane16, acc);
+    r0 += 2;
+  }
+  if (r0 < p) fold_batch<1, GDT, CONT>(gr, r0, e0, lane16, acc);
+}
+
+// Two vectors per lane (element offsets e0 and e1): both vectors' loads of
+// ranks r0 .. r0+B-1 in flight together, then the rank-order adds.
+template <int B, int GDT, bool CONT = false, class Grads>
+__device__ __forceinline__ void fold_batch2(const Grads& gr, int r0, int64_t e0, int64_t e1,
+                                            uint32_t lane16, float (&a)[kVec], float (&b)[kVec]) {
+  u32x4 qa[B], qb[B];
+#pragma unroll
+  for (int i = 0; i < B; ++i) {
+    qa[i] = ld_grad(gr.get(r0 + i) + e0, lane16);
+    qb[i] = ld_grad(gr.get(r0 + i) + e1, lane16);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (!CONT && r0 == 0) {
+    init8<GDT>(a, qa[0]);
+    init8<GDT>(b, qb[0]);
+  } else {
+    fold8<GDT>(a, qa[0]);
+    fold8<GDT>(b, qb[0]);
+  }
+#pragma unroll
+  for (int i = 1; i < B; ++i) {
+    fold8<GDT>(a, qa[i]);
+    fold8<GDT>(b, qb[i]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// MAXB caps the rank batch (8 keeps the small-shard kernel within the
+// registers of four waves per SIMD).
+template <int GDT, int MAXB = 16, bool CONT = false, class Grads>
+__device__ __forceinline__ void sum_ranks8x2(const Grads& gr, int p, int64_t e0, int64_t e1,
+                                             uint32_t lane16, float (&a)[kVec],
+                                             float (&b)[kVec]) {
+  int r0 = 0;
+  if constexpr (MAXB >= 16) {
+    for (; r0 + 16 <= p; r0 += 16) fold_batch2<16, GDT, CONT>(gr, r0, e0, e1, lane16, a, b);
+    if (r0 + 8 <= p) {
+      fold_batch2<8, GDT, CONT>(gr, r0, e0, e1, lane16, a, b);
+      r0 += 8;
+    }
+  } else {
+    static_assert(MAXB == 8, "rank batches of 16 or 8");
+    for (; r0 + 8 <= p; r0 += 8) fold_batch2<8, GDT, CONT>(gr, r0, e0, e1, lane16, a, b);
+  }
+  if (r0 + 4 <= p) {
+    fold_batch2<4, GDT, CONT>(gr, r0, e0, e1, lane16, a, b);
+    r0 += 4;
+  }
+  if (r0 + 2 <= p) {
+    fold_batch2<2, GDT, CONT>(gr, r0, e0, e1, lane16, a, b);
+    r0 += 2;
+  }
+  if (r0 < p) fold_batch2<1, GDT, CONT>(gr, r0, e0, e1, lane16, a, b);
+}
+
+// Rank-order mean of one element, kRankBatch loads in flight per batch.
+template <int GDT, class Grads>
+__device__ __forceinline__ float mean1(const Grads& gr, int p, int64_t e, float PF) {
+  float s = 0.0f;
+  int r0 = 0;
+  for (; r0 + kRankBatch <= p; r0 += kRankBatch) {
+    uint16_t q[kRankBatch];
+#pragma unroll
+    for (int b = 0; b < kRankBatch; ++b) q[b] = gr.get(r0 + b)[e];
+    __builtin_amdgcn_sched_barrier(0);
+    s = r0 == 0 ? widen1<GDT>(q[0]) : s + widen1<GDT>(q[0]);
+#pragma unroll
+    for (int b = 1; b < kRankBatch; ++b) s = s + widen1<GDT>(q[b]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (; r0 < p; ++r0) {
+    const float x = widen1<GDT>(gr.get(r0)[e]);
+    s = r0 == 0 ? x : s + x;
+  }
+  return s / PF;
+}
+
+// Adam + downcast of one lane's 8 elements at uniform element e0.  x holds
+// the fp32 gradient mean, or (DIVIDE) the rank sums, divided by P here.  The
+// sums are read, never written back: writing the quotients into the sum
+// registers before the update measurably worsens register allocation.
+template <int PDT, int FORM, bool PARAM = true, bool DIVIDE = false>
+__device__ __forceinline__ void adam8(const Consts& c, const float (&x)[kVec], float* w, float* m,
+                                      float* v, uint16_t* par, int64_t e0, uint32_t lane16,
+                                      uint32_t lane32) {
+  float* wb = w + e0;
+  float* mb = m + e0;
+  float* vb = v + e0;
+  const f32x4 w0 = ld_f32x4(wb, lane32), w1 = ld_f32x4(wb, lane32 + 16);
+  const f32x4 m0 = ld_state<kUsesM<FORM>>(mb, lane32), m1 = ld_state<kUsesM<FORM>>(mb, lane32 + 16);
+  const f32x4 v0 = ld_state<kUsesV<FORM>>(vb, lane32), v1 = ld_state<kUsesV<FORM>>(vb, lane32 + 16);
+  float W[kVec] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+  float M[kVec] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+  float V[kVec] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+  for (int j = 0; j < kVec; ++j) {
+    if constexpr (DIVIDE) {
+      adam1<FORM>(c, x[j] / c.PF, W[j], M[j], V[j]);
+    } else {
+      adam1<FORM>(c, x[j], W[j], M[j], V[j]);
+    }
+  }
+  st_f32x4(wb, lane32, f32x4{W[0], W[1], W[2], W[3]});
+  st_f32x4(wb, lane32 + 16, f32x4{W[4], W[5], W[6], W[7]});
+  st_state<kUsesM<FORM>>(mb, lane32, f32x4{M[0], M[1], M[2], M[3]});
+  st_state<kUsesM<FORM>>(mb, lane32 + 16, f32x4{M[4], M[5], M[6], M[7]});
+  st_state<kUsesV<FORM>>(vb, lane32, f32x4{V[0], V[1], V[2], V[3]});
+  st_state<kUsesV<FORM>>(vb, lane32 + 16, f32x4{V[4], V[5], V[6], V[7]});
+  if constexpr (PARAM)
+    st_u16x8(par + e0, lane16,
+             u32x4{narrow2<PDT>(W[0], W[1]), narrow2<PDT>(W[2], W[3]), narrow2<PDT>(W[4], W[5]),
+                   narrow2<PDT>(W[6], W[7])});
+}
+
+// adam8 for two vectors per lane: the state loads of both are issued
+// together, then the arithmetic and stores of each.
+template <int PDT, int FORM, bool DIVIDE = true, bool PARAM = true>
+__device__ __forceinline__ void adam8x2(const Consts& c, const float (&a)[kVec],
+                                        const float (&b)[kVec], float* w, float* m, float* v,
+                                        uint16_t* par, int64_t e0, int64_t e1, uint32_t lane16,
+                                        uint32_t lane32) {
+  f32x4 S[2][6];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int64_t e = q == 0 ? e0 : e1;
+    S[q][0] = ld_f32x4(w + e, lane32);
+    S[q][1] = ld_f32x4(w + e, lane32 + 16);
+    S[q][2] = ld_state<kUsesM<FORM>>(m + e, lane32);
+    S[q][3] = ld_state<kUsesM<FORM>>(m + e, lane32 + 16);
+    S[q][4] = ld_state<kUsesV<FORM>>(v + e, lane32);
+    S[q][5] = ld_state<kUsesV<FORM>>(v + e, lane32 + 16);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int64_t e = q == 0 ? e0 : e1;
+    const float(&x)[kVec] = q == 0 ? a : b;
+    float W[kVec] = {S[q][0].x, S[q][0].y, S[q][0].z, S[q][0].w,
+                     S[q][1].x, S[q][1].y, S[q][1].z, S[q][1].w};
+    float M[kVec] = {S[q][2].x, S[q][2].y, S[q][2].z, S[q][2].w,
+                     S[q][3].x, S[q][3].y, S[q][3].z, S[q][3].w};
+    float V[kVec] = {S[q][4].x, S[q][4].y, S[q][4].z, S[q][4].w,
+                     S[q][5].x, S[q][5].y, S[q][5].z, S[q][5].w};
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) {
+      if constexpr (DIVIDE) {
+        adam1<FORM>(c, x[j] / c.PF, W[j], M[j], V[j]);
+      } else {
+        adam1<FORM>(c, x[j], W[j], M[j], V[j]);
+      }
+    }
+    st_f32x4(w + e, lane32, f32x4{W[0], W[1], W[2], W[3]});
+    st_f32x4(w + e, lane32 + 16, f32x4{W[4], W[5], W[6], W[7]});
+    st_state<kUsesM<FORM>>(m + e, lane32, f32x4{M[0], M[1], M[2], M[3]});
+    st_state<kUsesM<FORM>>(m + e, lane32 + 16, f32x4{M[4], M[5], M[6], M[7]});
+    st_state<kUsesV<FORM>>(v + e, lane32, f32x4{V[0], V[1], V[2], V[3]});
+    st_state<kUsesV<FORM>>(v + e, lane32 + 16, f32x4{V[4], V[5], V[6], V[7]});
+    if constexpr (PARAM)
+      st_u16x8(par + e, lane16,
+               u32x4{narrow2<PDT>(W[0], W[1]), narrow2<PDT>(W[2], W[3]), narrow2<PDT>(W[4], W[5]),
+                     narrow2<PDT>(W[6], W[7])});
+  }
+}
+
+// The part of a shard that whole kGroupsMax chunks do not cover: the leftover
+// groups (two vectors of 8 elements per lane, 2 * kBlock vectors per piece) and the
+// scalar head and tail elements.  left0 is the first vector after the whole
+// chunks.  Whole chunks go round-robin, so blocks nfull % nblk, ... have one
+// chunk fewer than the rest: the pieces are dealt out starting there, then the
+// scalar elements go to the next block.  Both read the ranks in batches
+// (several loads in flight per lane): a piece is too small to batch over
+// groups, and one load at a time would cost a full memory round trip per rank.
+template <int GDT, int PDT, int FORM, int MAXB = 16, class Grads>
+__device__ __forceinline__ void fused_rest(const Grads& gr, int p, float* __restrict__ w,
+                                           float* __restrict__ m, float* __restrict__ v,
+                                           uint16_t* __restrict__ par, int64_t len, int64_t h,
+                                           int64_t nvec, int64_t left0, int64_t nfull,
+                                           const Consts& c, int64_t blk, int64_t nblk,
+                                           uint32_t lane16, uint32_t lane32) {
+  const int tid = threadIdx.x;
+  const int64_t first = nfull % nblk;
+  const int64_t me = (blk - first + nblk) % nblk;  // this block's rank in the deal
+  constexpr int64_t kPiece = 2 * kBlock;  // vectors per piece: two per lane
+  const int64_t npieces = (nvec - left0 + kPiece - 1) / kPiece;
+  for (int64_t i = me; i < npieces; i += nblk) {
+    const int64_t gb = left0 + i * kPiece;
+    const int64_t e0 = h + gb * kVec;
+    const int64_t e1 = e0 + static_cast<int64_t>(kBlock) * kVec;
+    if (gb + kBlock + tid < nvec) {
+      float a[kVec], b[kVec];
+      sum_ranks8x2<GDT, MAXB>(gr, p, e0, e1, lane16, a, b);
+      adam8x2<PDT, FORM>(c, a, b, w, m, v, par, e0, e1, lane16, lane32);
+    } else if (gb + tid < nvec) {
+      float g[kVec];
+      sum_ranks8<GDT>(gr, p, e0, lane16, g);
+      adam8<PDT, FORM, true, true>(c, g, w, m, v, par, e0, lane16, lane32);
+    }
+  }
+  if (me == npieces % nblk) {
+    const int64_t t0 = h + nvec * kVec;
+    const int64_t nsc = h + (len - t0);
+    for (int64_t i = tid; i < nsc; i += kBlock) {
+      const int64_t e = i < h ? i : t0 + (i - h);
+      const float g = mean1<GDT>(gr, p, e, c.PF);
+      float W = w[e], M = ld_state1<kUsesM<FORM>>(m + e), V = ld_state1<kUsesV<FORM>>(v + e);
+      adam1<FORM>(c, g, W, M, V);
+      w[e] = W;
+      st_state1<kUsesM<FORM>>(m + e, M);
+      st_state1<kUsesV<FORM>>(v + e, V);
+      par[e] = narrow1<PDT>(W);
+    }
+  }
+}
+
+// A range of elements of one step: gradient pointers, fp32 state and working
+// copy at the range's first element, the vector-group head, and its blocks.
+template <class Grads>
+struct Range {
+  Grads gr;
+  float* w;
+  float* m;
+  float* v;
+  uint16_t* par;
+  int64_t len;
+  int head;
+  int64_t blk, nblk;
+};
+
+// The chunk table of the multi-tensor step: one item per entry, one block
+// each.  The block stages the entry's P gradient pointers and its piece
+// descriptor in LDS.
+struct TableSrc {
+  const MtPiece* pieces;
+  const uint16_t* const* gptrs;  // npieces * p pointers, piece-major
+  const MtChunk* chunks;
+  int64_t nchunks;
+  int64_t chunk_elems;
+  int p;
+  __device__ __forceinline__ int64_t first() const { return blockIdx.x; }
+  __device__ __forceinline__ int64_t count() const { return nchunks; }
+  __device__ __forceinline__ int64_t stride() const { return gridDim.x; }
+  __device__ __forceinline__ Range<LdsGrads> open(int64_t ch) const {
+    __shared__ const uint16_t* s_g[kMaxP];
+    __shared__ MtPiece s_piece;
+    const MtChunk cc = chunks[ch];
+    __syncthreads();  // the previous entry's readers of s_g / s_piece are done
+    for (int r = threadIdx.x; r < p; r += kBlock)
+      s_g[r] = gptrs[static_cast<int64_t>(cc.piece) * p + r] + cc.start;
+    if (threadIdx.x == 0) s_piece = pieces[cc.piece];
+    __syncthreads();
+    const int64_t rest = s_piece.len - cc.start;
+    const int64_t len = rest < chunk_elems ? rest : chunk_elems;
+    const int head = (s_piece.head - static_cast<int>(cc.start & 7)) & 7;
+    return Range<LdsGrads>{LdsGrads{s_g},
+                           uniform_t(s_piece.w) + cc.start,
+                           uniform_t(s_piece.m) + cc.start,
+                           uniform_t(s_piece.v) + cc.start,
+                           uniform_t(s_piece.param) + cc.start,
+                           len, head, 0, 1};
+  }
+};
+
+// Whole chunks used out of nfull: whole rounds over the nblk blocks, plus the
+// last partial round when it fills at least half of the blocks.  A smaller
+// last round goes to the rank-batched pieces instead, which every block
+// shares (a shard of 109 chunks on 256 blocks would otherwise leave 147 CUs
+// idle while 109 run one chunk each).
+__device__ __forceinline__ int64_t whole_chunks(int64_t nfull, int64_t nblk) {
+  const int64_t rem = nfull % nblk;
+  return 2 * rem >= nblk ? nfull : nfull - rem;
+}
+
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+template <class F>
+void with_dt(int dt, F&& f) {
+  if (dt == kF16) f(IC<kF16>{}); else f(IC<kBF16>{});
+}
+
+template <class F>
+void with_form(int form, F&& f) {
+  switch (form) {
+    case kStandard: f(IC<kStandard>{}); break;
+    case kPage1Literal: f(IC<kPage1Literal>{}); break;
+    case kSgd: f(IC<kSgd>{}); break;
+    default: f(IC<kSgdMomentum>{}); break;
+  }
+}
+
+// Kernel-argument pointer tables of 64 or kKernargP ranks.
+template <class F>
+void with_pmax(int p, F&& f) {
+  if (p <= 64) f(IC<64>{});
+  else f(IC<kKernargP>{});
+}
+
+}  // namespace
+}  // namespace zs

@@ -1,0 +1,180 @@
+// zs_fused.h -- the single-tensor fused step kernels; zs_fused_f16.hip and
+// zs_fused_bf16.hip instantiate them per gradient dtype.
+
+#pragma once
+
+#include "zs_device.h"
+
+namespace zs {
+namespace {
+
+// Single-tensor fused step, one workgroup per CU.  The loop over whole chunks
+// (nearly all of the bytes) is written out in the kernel body instead of going
+// through read_chunk / update_chunk: when the per-group sums cross a function
+// boundary by reference, the callee is optimised on its own before inlining
+// and the compiler peels the first rank out of the rank loop; the resulting
+// schedule measured about 11% slower on MI355X (3.17 ms against 2.85 ms on a
+// 117M-element, 64-rank shard) with bit-identical results.  Kept in this
+// shape, the rank loop tests r == 0 per group and keeps a single loop body.
+template <int GDT, int PDT, int FORM, int PMAX>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fused_kernel(GradArgs<PMAX> ga, int p, float* __restrict__ w, float* __restrict__ m,
+                  float* __restrict__ v, uint16_t* __restrict__ par, int64_t len, int head,
+                  Consts c, const void* rank_table) {
+  (void)ga;  // read through the kernel-argument segment, see kernarg_grads()
+  const ArgGrads gr = rank_grads(rank_table);
+  const int64_t h = head < len ? head : len;
+  const int64_t nvec = (len - h) / kVec;
+  const uint32_t lane16 = threadIdx.x * 16u;
+  const uint32_t lane32 = threadIdx.x * 32u;
+  constexpr int64_t kFull = static_cast<int64_t>(kBlock) * kGroupsMax;
+  const int64_t nfull = whole_chunks(nvec / kFull, gridDim.x);
+  for (int64_t ch = blockIdx.x; ch < nfull; ch += gridDim.x) {
+    const int64_t g0 = ch * kFull;
+    float s[kGroupsMax][kVec];
+    // read phase: rank-major, kLoadBatch loads in flight per batch
+    for (int r = 0; r < p; ++r) {
+      const uint16_t* base = gr.get(r) + h + g0 * kVec;
+      // Group 0 alone first, and used before the other loads go out: the
+      // first access to this rank's pages takes the address-translation miss
+      // with one load per wave waiting on it, not a whole batch (a batch
+      // queued behind the miss fills the per-CU translation queue and stalls
+      // every wave's loads).
+      {
+        const u32x4 q0 = ld_grad(base, lane16);
+        __builtin_amdgcn_sched_barrier(0);
+        if (r == 0) {
+          init8<GDT>(s[0], q0);
+        } else {
+          fold8<GDT>(s[0], q0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      {  // groups 1 .. kLoadBatch-1
+        u32x4 q[kLoadBatch - 1];
+#pragma unroll
+        for (int u = 0; u < kLoadBatch - 1; ++u)
+          q[u] = ld_grad(base + static_cast<int64_t>(1 + u) * kBlock * kVec, lane16);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < kLoadBatch - 1; ++u) {
+          if (r == 0) {
+            init8<GDT>(s[1 + u], q[u]);
+          } else {
+            fold8<GDT>(s[1 + u], q[u]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int u0 = kLoadBatch; u0 < kGroupsMax; u0 += kLoadBatch) {
+        u32x4 q[kLoadBatch];
+#pragma unroll
+        for (int u = 0; u < kLoadBatch; ++u)
+          q[u] = ld_grad(base + static_cast<int64_t>(u0 + u) * kBlock * kVec, lane16);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < kLoadBatch; ++u) {
+          if (r == 0) {
+            init8<GDT>(s[u0 + u], q[u]);
+          } else {
+            fold8<GDT>(s[u0 + u], q[u]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // update phase: mean, Adam, stores, group by group
+#pragma unroll
+    for (int u = 0; u < kGroupsMax; ++u) {
+      const int64_t e0 = h + (g0 + static_cast<int64_t>(u) * kBlock) * kVec;
+      float* wb = w + e0;
+      float* mb = m + e0;
+      float* vb = v + e0;
+      const f32x4 w0 = ld_f32x4(wb, lane32), w1 = ld_f32x4(wb, lane32 + 16);
+      const f32x4 m0 = ld_state<kUsesM<FORM>>(mb, lane32), m1 = ld_state<kUsesM<FORM>>(mb, lane32 + 16);
+      const f32x4 v0 = ld_state<kUsesV<FORM>>(vb, lane32), v1 = ld_state<kUsesV<FORM>>(vb, lane32 + 16);
+      float W[kVec] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      float M[kVec] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+      float V[kVec] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+      for (int j = 0; j < kVec; ++j) adam1<FORM>(c, s[u][j] / c.PF, W[j], M[j], V[j]);
+      st_f32x4(wb, lane32, f32x4{W[0], W[1], W[2], W[3]});
+      st_f32x4(wb, lane32 + 16, f32x4{W[4], W[5], W[6], W[7]});
+      st_state<kUsesM<FORM>>(mb, lane32, f32x4{M[0], M[1], M[2], M[3]});
+      st_state<kUsesM<FORM>>(mb, lane32 + 16, f32x4{M[4], M[5], M[6], M[7]});
+      st_state<kUsesV<FORM>>(vb, lane32, f32x4{V[0], V[1], V[2], V[3]});
+      st_state<kUsesV<FORM>>(vb, lane32 + 16, f32x4{V[4], V[5], V[6], V[7]});
+      st_u16x8(par + e0, lane16,
+               u32x4{narrow2<PDT>(W[0], W[1]), narrow2<PDT>(W[2], W[3]),
+                     narrow2<PDT>(W[4], W[5]), narrow2<PDT>(W[6], W[7])});
+    }
+  }
+  fused_rest<GDT, PDT, FORM>(gr, p, w, m, v, par, len, h, nvec, nfull * kFull, nfull, c,
+                             blockIdx.x, gridDim.x, lane16, lane32);
+}
+
+// Single-tensor fused step for shards under half a whole chunk per CU, where
+// fused_kernel would run no whole chunk at all: the same two-vector pieces,
+// dealt over four workgroups per CU (four waves per SIMD, rank batches of at
+// most 8 so that no register spills).  On the 16-rank, 6.25M-element shards
+// this is 4% faster than one workgroup per CU.
+template <int GDT, int PDT, int FORM, int PMAX>
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kSmallWaves)))
+void small_kernel(GradArgs<PMAX> ga, int p, float* __restrict__ w, float* __restrict__ m,
+                  float* __restrict__ v, uint16_t* __restrict__ par, int64_t len, int head,
+                  Consts c, const void* rank_table) {
+  (void)ga;  // read through the kernel-argument segment, see kernarg_grads()
+  const ArgGrads gr = rank_grads(rank_table);
+  const int64_t h = head < len ? head : len;
+  const int64_t nvec = (len - h) / kVec;
+  fused_rest<GDT, PDT, FORM, 8>(gr, p, w, m, v, par, len, h, nvec, 0, 0, c, blockIdx.x,
+                                gridDim.x, threadIdx.x * 16u, threadIdx.x * 32u);
+}
+
+}  // namespace
+
+template <int GDT>
+hipError_t launch_fused_g(const FusedLaunch& a) {
+  // fused_kernel: one workgroup per CU (one wave per SIMD).  A shard under
+  // half a whole chunk per CU would give it no whole chunk: small_kernel
+  // deals that shard's pieces over kSmallWaves workgroups per CU, one piece
+  // (two vectors per lane) per workgroup at least.
+  const int64_t h = a.head < a.len ? a.head : a.len;
+  const int64_t nvec = (a.len - h) / kVec;
+  const int64_t cu = cu_count();
+  constexpr int64_t kFull = static_cast<int64_t>(kBlock) * kGroupsMax;
+  const bool small = 2 * (nvec / kFull) < cu;
+  int64_t grid, cap;
+  if (small) {
+    grid = (nvec + 2 * kBlock - 1) / (2 * kBlock);
+    cap = cu * kSmallWaves;
+  } else {
+    grid = (nvec + kBlock - 1) / kBlock;
+    cap = cu;
+  }
+  if (grid > cap) grid = cap;
+  if (grid < 1) grid = 1;
+  with_dt(a.pdt, [&](auto H) {
+    with_form(a.form, [&](auto F) {
+      // with a device rank table the kernel arguments carry no pointers: the
+      // smallest instance
+      with_pmax(a.rank_table ? 1 : a.p, [&](auto PM) {
+        constexpr int PMAX = decltype(PM)::value;
+        GradArgs<PMAX> ga;
+        for (int r = 0; r < PMAX; ++r) ga.g[r] = !a.rank_table && r < a.p ? a.grads[r] : nullptr;
+        if (small)
+          small_kernel<GDT, decltype(H)::value, decltype(F)::value, PMAX>
+              <<<dim3(static_cast<unsigned>(grid)), dim3(kBlock), 0, a.stream>>>(
+                  ga, a.p, a.w, a.m, a.v, a.param, a.len, a.head, a.c, a.rank_table);
+        else
+          fused_kernel<GDT, decltype(H)::value, decltype(F)::value, PMAX>
+              <<<dim3(static_cast<unsigned>(grid)), dim3(kBlock), 0, a.stream>>>(
+                  ga, a.p, a.w, a.m, a.v, a.param, a.len, a.head, a.c, a.rank_table);
+      });
+    });
+  });
+  return hipGetLastError();
+}
+
+}  // namespace zs

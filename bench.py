@@ -32,8 +32,11 @@ if ROOT not in sys.path:
 
 METRIC = "shard elements/s and achieved HBM GB/s (% of MI355X peak), fused shard Adam"
 HBM_PEAK_GBS = 8000.0
-KERNEL_SOURCES = [os.path.join(ROOT, "adam_zs_shard_amd", "csrc", f)
-                  for f in ("zs_kernels.hip", "zs_capi.cpp", "zs_internal.h")]
+CSRC = os.path.join(ROOT, "adam_zs_shard_amd", "csrc")
+# the step's device code and launch logic (not the host offload or the probes)
+KERNEL_SOURCES = [os.path.join(CSRC, f) for f in (
+    "zs_device.h", "zs_fused.h", "zs_fused_f16.hip", "zs_fused_bf16.hip", "zs_table.hip",
+    "zs_unfused.hip", "zs_common.hip", "zs_internal.h", "zs_capi.cpp")]
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
 
 
@@ -106,11 +109,29 @@ def cpu_baseline(gdt: str, pdt: str, grads_host, w, m, v, threads: int, form: st
 
 
 def host_threads() -> int:
+    """The host CPUs this process may use: its affinity mask, capped by
+    OMP_NUM_THREADS when that is set (the CPU share a GPU host gives one
+    GPU's jobs)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
         n = os.cpu_count() or 1
-    return max(1, min(16, n))
+    try:
+        cap = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        cap = 0
+    return max(1, min(n, cap) if cap > 0 else n)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
 
 
 def _state(wl, w):
@@ -226,7 +247,9 @@ def bench_unfused(args):
 
 
 def _cpu_leg(args, wl, grads, w, m, v, label):
-    """The oracle on a contiguous sample of one shard's elements."""
+    """The oracle on a contiguous sample of one shard's elements: once on all
+    the host threads this process may use, once on one thread (an eighth of
+    the sample)."""
     import numpy as np
     import torch
 
@@ -239,9 +262,19 @@ def _cpu_leg(args, wl, grads, w, m, v, label):
     vh = v[a0:a0 + S].cpu().numpy().copy() if v is not None else np.zeros(S, np.float32)
     thr = host_threads()
     secs = cpu_baseline(wl.grad_dtype, wl.param_dtype, gh, wh, mh, vh, thr, wl.form)
+    S1 = max(1, S // 8)
+    secs1 = cpu_baseline(wl.grad_dtype, wl.param_dtype, [g[:S1] for g in gh], wh[:S1].copy(),
+                         mh[:S1].copy(), vh[:S1].copy(), 1, wl.form)
+    try:
+        visible = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        visible = os.cpu_count() or 1
     return {"value": S / secs, "unit": "elements/s", "cores": thr, "kind": "oracle",
             "sample": f"{S} contiguous elements from the middle of {label} ({wl.p} ranks), one "
-                      f"step, {secs:.2f} s wall on {thr} threads"}
+                      f"step, {secs:.2f} s wall on {thr} threads; one thread: the first {S1} "
+                      f"of them, {secs1:.2f} s",
+            "one_thread": S1 / secs1, "cpu_model": cpu_model(), "cpus_visible": visible,
+            "os_cpu_count": os.cpu_count()}
 
 
 def bench_multi(args):
@@ -258,15 +291,9 @@ def bench_multi(args):
     L = e[k] - s[k]
     dev = "cuda"
     td = {"f16": torch.float16, "bf16": torch.bfloat16}
-    if args.chunk <= 0:
-        whole = 28 * 256 * 8
-        ncu = torch.cuda.get_device_properties(0).multi_processor_count
-        # one chunk per CU for a single-piece shard; four for shards of several
-        # pieces, whose chunks end unevenly at the piece boundaries
-        npieces = len(z.zs_plan_chunks(numel, wl.p, k, whole)[0])
-        split = ncu if npieces == 1 else 4 * ncu
-        per = -(-L // split)
-        args.chunk = whole if L >= 2 * whole * ncu else -(-per // 2048) * 2048
+    if args.chunk <= 0:  # the library's chunk rule for this shard
+        npieces = len(z.zs_plan_chunks(numel, wl.p, k, 8)[0])
+        args.chunk = z.zs_mt_chunk_elems(L, npieces)
     pieces, nchunks = z.zs_plan_chunks(numel, wl.p, k, args.chunk)
     print(f"[bench] {wl.name}: N={wl.n} P={wl.p} k={k} L={L} pieces={len(pieces)} "
           f"chunks={nchunks} chunk_elems={args.chunk}", file=sys.stderr, flush=True)
@@ -285,24 +312,19 @@ def bench_multi(args):
             for (t, to, so, ln) in pieces]
     stream = torch.cuda.current_stream()
     # one table for the whole shard, or (--bucket-elems) one per bucket of
-    # consecutive pieces holding at least that many elements
-    groups, cur, size = [], [], 0
-    for i, pc in enumerate(pieces):
-        cur.append(i)
-        size += pc[3]
-        if args.bucket_elems > 0 and size >= args.bucket_elems:
-            groups.append(cur)
-            cur, size = [], 0
-    if cur:
-        groups.append(cur)
+    # consecutive pieces holding at least that many elements (zs_plan_buckets),
+    # each with the chunk length the library gives for the bucket on its own
+    if args.bucket_elems > 0:
+        of, nb = z.zs_plan_buckets(pieces, args.bucket_elems)
+        groups = [[i for i in range(len(pieces)) if of[i] == b] for b in range(nb)]
+    else:
+        groups = [list(range(len(pieces)))]
     tables, keep = [], []
-    ncu = torch.cuda.get_device_properties(0).multi_processor_count
     for g in groups:
         sub = [pieces[i] for i in g]
         chunk = args.chunk
-        if len(groups) > 1:  # a bucket is spread over all CUs on its own
-            lb = sum(pc[3] for pc in sub)
-            chunk = min(args.chunk, max(2048, -(-(-(-lb // ncu)) // 2048) * 2048))
+        if len(groups) > 1:
+            chunk = z.zs_mt_chunk_elems(sum(pc[3] for pc in sub), 1)
         nch = sum((ln + chunk - 1) // chunk for (_, _, _, ln) in sub)
         nb = z.zs_mt_workspace_bytes(len(sub), nch, wl.p)
         ws = torch.empty(nb, dtype=torch.uint8, device=dev)
@@ -311,25 +333,27 @@ def bench_multi(args):
                                      wl.param_dtype, chunk, ws, nb, stream=stream.cuda_stream))
     torch.cuda.synchronize()
 
-    def launches(hp, st):
-        for tb in tables:
-            z.zs_fused_shard_step_multi(tb, hp, stream=st)
-
     if args.graph:
-        # replay reuses the captured arguments: only forms whose constants do
-        # not change with the step
-        if z.FORMS[wl.form] not in (z.ZS_SGD, z.ZS_SGD_MOMENTUM):
-            print("--graph needs --form sgd or sgd_momentum (Adam's bias corrections change "
-                  "every step)", file=sys.stderr)
-            sys.exit(2)
-        hp0 = z.hparams(wl.lr, wl.beta1, wl.beta2, wl.eps, 1, wl.form)
-        launches(hp0, stream.cuda_stream)   # first call outside capture
+        # captured once and replayed: the step constants come from a device
+        # step table that a one-thread kernel in the graph advances
+        nsteps = args.warmup + args.steps + 1
+        nbytes = z.zs_step_table_bytes(nsteps)
+        st_buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        keep.append(st_buf)
+        steps = z.zs_step_table_init(z.hparams(wl.lr, wl.beta1, wl.beta2, wl.eps, 1, wl.form),
+                                     wl.p, nsteps, st_buf, nbytes, stream=stream.cuda_stream)
+
+        def launches_dev(st):
+            for tb in tables:
+                z.zs_fused_shard_step_multi_dev(tb, steps, stream=st)
+            z.zs_step_table_advance(steps, stream=st)
+
         graph = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(stream)
         with torch.cuda.stream(side):
             with torch.cuda.graph(graph):
-                launches(hp0, torch.cuda.current_stream().cuda_stream)
+                launches_dev(torch.cuda.current_stream().cuda_stream)
         stream.wait_stream(side)
         torch.cuda.synchronize()
 
@@ -337,8 +361,9 @@ def bench_multi(args):
             graph.replay()
     else:
         def step(i):
-            launches(z.hparams(wl.lr, wl.beta1, wl.beta2, wl.eps, i + 1, wl.form),
-                     stream.cuda_stream)
+            hp = z.hparams(wl.lr, wl.beta1, wl.beta2, wl.eps, i + 1, wl.form)
+            for tb in tables:
+                z.zs_fused_shard_step_multi(tb, hp, stream=stream.cuda_stream)
 
     ms, wall = _time_steps(step, args.steps, args.warmup, stream)
     cpu = None if args.no_cpu_baseline else _cpu_leg(args, wl, grads, w, m, v, f"shard {k}")
@@ -457,6 +482,97 @@ def bench_cpu_offload(args):
     }), flush=True)
 
 
+def bench_offload(args):
+    """The optimizer offload of one shard on one GPU (zs_offload_step): GPU
+    rank mean rounded to 16 bits, bucket by bucket, copied to pinned host
+    memory; the update on the host CPU; the 16-bit parameters copied back.
+    Timed per step with the plain schedule and with the delayed parameter
+    update (the update of step t-1's gradient overlapping the GPU mean and
+    copy of step t's), next to each part timed alone."""
+    import numpy as np
+    import torch
+
+    from adam_zs_shard_amd import zshard as z
+    from zs_synth import WORKLOADS, seed_for
+    from zs_synth.gen import normal
+
+    wl = WORKLOADS[args.workload]
+    k = wl.shards[-1]
+    M, s, e = z.zs_plan_shards(wl.n, wl.p)
+    L = e[k] - s[k]
+    thr = host_threads()
+    bucket = args.bucket_elems if args.bucket_elems > 0 else 1 << 23
+    td = {"f16": torch.float16, "bf16": torch.bfloat16}
+    dt = td[wl.grad_dtype]
+    print(f"[bench] offload {wl.name}: shard {k}, {L} elements, P={wl.p}, buckets of {bucket}, "
+          f"{thr} threads", file=sys.stderr, flush=True)
+    grads = [normal(L, wl.grad_std, seed_for(20261202, r, 1, 1, k), dt, "cuda")
+             for r in range(wl.p)]
+    param = torch.empty(L, dtype=td[wl.param_dtype], device="cuda")
+    g16_dev = torch.empty(L, dtype=dt, device="cuda")
+    partial = torch.empty(L, device="cuda") if wl.p > z.ZS_KERNARG_P else None
+    pin = dict(pin_memory=True)
+    g16_host = [torch.empty(L, dtype=dt, **pin) for _ in range(2)]
+    w = torch.empty(L, **pin)
+    w.copy_(normal(L, wl.w_std, seed_for(20261202, -1, 0, 2, k)))
+    f = z.FORMS[wl.form]
+    m = torch.zeros(L, **pin) if f != z.ZS_SGD else None
+    v = torch.zeros(L, **pin) if f in (z.ZS_ADAM_STANDARD, z.ZS_ADAM_PAGE1_LITERAL) else None
+    param_host = torch.empty(L, dtype=td[wl.param_dtype], **pin)
+    cs = torch.cuda.current_stream()
+    d2h, h2d = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    count = [0]
+
+    def step(mode, slot):
+        count[0] += 1
+        hp = z.hparams(wl.lr, wl.beta1, wl.beta2, wl.eps, count[0], wl.form)
+        z.zs_offload_step(wl.n, wl.p, k, grads, param, g16_dev, g16_host, w, m, v, param_host,
+                          hp, mode, slot, grad_base=s[k], param_base=s[k], partial=partial,
+                          bucket_elems=bucket, threads=thr, compute_stream=cs, d2h_stream=d2h,
+                          h2d_stream=h2d)
+
+    def timed(fn, n):
+        t0 = time.perf_counter()
+        for i in range(n):
+            fn(i)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / n
+
+    for i in range(args.warmup):
+        step(z.ZS_OFFLOAD_PLAIN, 0)
+    plain = timed(lambda i: step(z.ZS_OFFLOAD_PLAIN, 0), args.steps)
+    step(z.ZS_OFFLOAD_RECEIVE, 0)
+    delayed = timed(lambda i: step(z.ZS_OFFLOAD_DELAYED, (i + 1) % 2), args.steps)
+    # the parts alone
+    hp1 = z.hparams(wl.lr, wl.beta1, wl.beta2, wl.eps, 1, wl.form)
+    mean_t = timed(lambda i: z.zs_reduce_scatter_mean_local16(grads, wl.n, wl.p, k, g16_dev,
+                                                              grad_base=s[k], partial=partial),
+                   args.steps)
+    d2h_t = timed(lambda i: g16_host[0].copy_(g16_dev, non_blocking=True), args.steps)
+    cpu_t = timed(lambda i: z.zs_cpu_adam_step(g16_host[0], wl.grad_dtype, w, m, v, param_host,
+                                               wl.param_dtype, L, hp1, threads=thr), args.steps)
+    h2d_t = timed(lambda i: param.copy_(param_host, non_blocking=True), args.steps)
+    parts = mean_t + d2h_t + cpu_t + h2d_t
+    print(json.dumps({
+        "metric": "shard elements/s, optimizer offload on one GPU (GPU mean -> host update -> "
+                  "parameters back)",
+        "value": L / delayed, "unit": "elements/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": delayed * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "shard": k, "elems_per_step": L, "ranks": wl.p,
+                   "grad_dtype": wl.grad_dtype, "param_dtype": wl.param_dtype,
+                   "adam_form": wl.form, "bucket_elems": bucket, "cpu_threads": thr,
+                   "cpu_model": cpu_model()},
+        "offload": {"plain_ms": plain * 1e3, "delayed_ms": delayed * 1e3,
+                    "parts_ms": {"gpu_mean16": mean_t * 1e3, "d2h": d2h_t * 1e3,
+                                 "cpu_update": cpu_t * 1e3, "h2d": h2d_t * 1e3},
+                    "sum_of_parts_ms": parts * 1e3,
+                    "d2h_gbs": 2 * L / d2h_t / 1e9, "h2d_gbs": 2 * L / h2d_t / 1e9,
+                    "cpu_update_gbs": (2 + z.BYTES_PER_ELEM[f]) * L / cpu_t / 1e9},
+    }), flush=True)
+
+
 def copy_probe(nbytes: int = 1 << 31, reps: int = 10):
     """A plain device copy of known size (torch's copy kernel), used to
     calibrate rocprofv3's FETCH_SIZE / WRITE_SIZE counters: each dispatch
@@ -474,6 +590,78 @@ def copy_probe(nbytes: int = 1 << 31, reps: int = 10):
     print(json.dumps({"copy_probe_bytes_read": nbytes, "copy_probe_bytes_written": nbytes,
                       "dispatches": reps, "seconds_per_copy": dt,
                       "gbs_read_plus_write": 2 * nbytes / dt / 1e9}), flush=True)
+
+
+def ceiling(args):
+    """HBM ceilings of this part from the stream probes: for each mix, the
+    best of several grid sizes (10 timed launches each after 2 warm-ups, HIP
+    events on the probe's stream); every launch moves about 6 GB."""
+    import ctypes as C
+
+    import torch
+
+    from adam_zs_shard_amd import _build
+
+    if not os.path.exists(_build.PROBE_PATH):
+        raise RuntimeError(f"{_build.PROBE_PATH} is not built; run __graft_entry__.build()")
+    P = C.CDLL(_build.PROBE_PATH)
+    P.zsp_stream.argtypes = [C.c_int32, C.c_void_p, C.c_void_p, C.c_int64, C.c_int64, C.c_int32,
+                             C.c_void_p, C.c_void_p]
+    P.zsp_stream.restype = C.c_int32
+    P.zsp_streams.argtypes = [C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_int32)]
+    P.zsp_streams.restype = C.c_int32
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    mixes = [("read", 0, None), ("copy", 1, None), ("mix_10_1", 4, 154), ("mix_22_7", 3, 58),
+             ("mix_2_1", 2, 42), ("phased_read", 5, None), ("phased_copy", 6, None),
+             ("phased_10_1", 9, 154), ("phased_22_7", 8, 58), ("phased_2_1", 7, 42)]
+    out = {}
+    for name, mix, bpe in mixes:
+        nr, nw = C.c_int32(), C.c_int32()
+        assert P.zsp_streams(mix, C.byref(nr), C.byref(nw)) == 0
+        nstreams = nr.value + nw.value
+        sb = (6_000_000_000 // nstreams) // (1 << 20) * (1 << 20)
+        nvec = sb // 16
+        src = torch.empty(nr.value * sb, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        dst = torch.empty(max(nw.value, 1) * sb if nw.value else 16, dtype=torch.uint8,
+                          device="cuda")
+        moved = 16 * nvec * nstreams
+        best, sweep = None, {}
+        for per_cu in ((1,) if name.startswith("phased") else (1, 2, 4, 8)):
+            grid = ncu * per_cu
+
+            def launch():
+                rc = P.zsp_stream(mix, src.data_ptr(), dst.data_ptr() if nw.value else None, sb,
+                                  nvec, grid, sink.data_ptr(), stream.cuda_stream)
+                assert rc == 0, f"probe {name} failed ({rc})"
+
+            for _ in range(2):
+                launch()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(10):
+                launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / 10
+            gbs = moved / (ms / 1e3) / 1e9
+            sweep[f"{per_cu}_per_cu"] = round(gbs, 1)
+            if best is None or gbs > best[0]:
+                best = (gbs, per_cu, ms)
+        out[name] = {"streams_read": nr.value, "streams_written": nw.value,
+                     "bytes_per_launch": moved, "best_gbs": round(best[0], 1),
+                     "best_frac_of_8tbs": round(best[0] / HBM_PEAK_GBS, 4),
+                     "best_workgroups_per_cu": best[1], "best_ms": round(best[2], 4),
+                     "gbs_by_workgroups_per_cu": sweep, "step_bytes_per_element": bpe}
+        print(f"[ceiling] {name}: {best[0]:.0f} GB/s ({best[1]} workgroups per CU)",
+              file=sys.stderr, flush=True)
+        del src, dst
+        torch.cuda.empty_cache()
+    print(json.dumps({"ceiling": out, "peak_gbs": HBM_PEAK_GBS, "cus": ncu}), flush=True)
 
 
 def main():
@@ -503,11 +691,17 @@ def main():
                     help="chunk-table workloads: one launch per bucket of consecutive pieces "
                          "holding at least this many elements (0: one launch per step)")
     ap.add_argument("--graph", action="store_true",
-                    help="chunk-table workloads, SGD forms: capture the step's launches in a "
-                         "HIP graph once and time its replays")
+                    help="chunk-table workloads: capture the step's launches in a HIP graph once "
+                         "(step constants read from a device step table) and time its replays")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="time only the bandwidth probes (libzsprobe): pure reads, a copy, and "
+                         "the read:write mixes of 154, 58 and 42 bytes per element")
     ap.add_argument("--cpu-offload", action="store_true",
                     help="time the host-CPU offload update (zs_cpu_adam_step) of the "
                          "workload's shard instead of the GPU step; no GPU needed")
+    ap.add_argument("--offload", action="store_true",
+                    help="time the optimizer offload on one GPU (zs_offload_step), plain and "
+                         "with the delayed parameter update, next to its parts")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain 2 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -544,6 +738,13 @@ def main():
         sys.exit(1)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.ceiling:
+        ceiling(args)
+        return
+    if args.offload:
+        z.lib()
+        bench_offload(args)
         return
 
     z.lib()  # fails loudly if the HIP library is not built

@@ -34,12 +34,12 @@ def _declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert len(names) == 12 and sorted(names) == sorted(z.EXPORTS)
+    assert len(names) == 22 and sorted(names) == sorted(z.EXPORTS)
     L = z.lib()
     for n in names:
         assert hasattr(L, n), n
     assert sorted(z.EXPORTS) == names
-    assert z.zs_version() == 1
+    assert z.zs_version() == 2
     for st in range(8):
         assert z.zs_status_string(st).startswith("ZS_")
     assert z.zs_status_string(99) == "ZS_ERR_UNKNOWN"
@@ -104,18 +104,21 @@ no_device = pytest.mark.skipif(_HAVE_GPU, reason="fake device addresses: CPU-onl
 
 
 def _fused(n=1000, p=4, k=1, grads=None, w=FAKE, m=FAKE + (1 << 30), v=FAKE + (2 << 30),
-           param=FAKE + (3 << 30), hp=HP, gdt=z.ZS_F16, pdt=z.ZS_F16, grad_base=0, param_base=0):
+           param=FAKE + (3 << 30), hp=HP, gdt=z.ZS_F16, pdt=z.ZS_F16, grad_base=0, param_base=0,
+           workspace=None, workspace_bytes=0):
     if grads is None:
         grads = [FAKE + ((4 + r) << 30) for r in range(p)]
     return z.zs_fused_shard_step(n, p, k, grads, w, m, v, param, hp, grad_base=grad_base,
                                  param_base=param_base, grad_dtype=gdt, param_dtype=pdt,
+                                 workspace=workspace, workspace_bytes=workspace_bytes,
                                  check=False)
 
 
 @no_device
 def test_fused_argument_errors():
     assert _fused(p=0) == z.ZS_ERR_ARG
-    assert _fused(p=257, grads=[FAKE] * 257) == z.ZS_ERR_ARG
+    assert _fused(p=1025, grads=[FAKE + (8 << 30) + (r << 20) for r in range(1025)]) == \
+        z.ZS_ERR_ARG
     assert _fused(k=4) == z.ZS_ERR_ARG
     assert _fused(k=-1) == z.ZS_ERR_ARG
     assert _fused(n=-5) == z.ZS_ERR_ARG
@@ -275,3 +278,191 @@ def test_multi_step_checks_state_mask():
     assert step(z.ZS_STATE_M, "sgd_momentum") == z.ZS_ERR_HIP
     assert step(0, "sgd_momentum") == z.ZS_ERR_NULL
     assert step(0, "sgd") == z.ZS_ERR_HIP
+
+
+def test_workspace_bytes_for_many_ranks():
+    assert z.ZS_MAX_P == 1024 and z.ZS_KERNARG_P == 256
+    for p in (1, 64, 256):
+        assert z.zs_shard_workspace_bytes(p) == 0
+    assert z.zs_shard_workspace_bytes(257) == 2304       # 8 * 257 rounded up to 256
+    assert z.zs_shard_workspace_bytes(512) == 4096
+    assert z.zs_shard_workspace_bytes(1024) == 8192
+    assert z.zs_shard_workspace_bytes(1025) == 0
+    assert z.zs_shard_workspace_bytes(0) == 0
+
+
+@no_device
+def test_many_ranks_need_a_workspace():
+    # 512 ranks: the rank pointers go through a device workspace
+    n, p, k = 100_000, 512, 7
+    g = [FAKE + (8 << 30) + (r << 24) for r in range(p)]   # clear of w, m, v and param
+    ws = FAKE + (3 << 30) + (1 << 20)     # clear of the working copy's used slice
+    assert _fused(n=n, p=p, k=k, grads=g) == z.ZS_ERR_CAPACITY               # none given
+    assert _fused(n=n, p=p, k=k, grads=g, workspace=ws, workspace_bytes=4095) == \
+        z.ZS_ERR_CAPACITY                                                      # too small
+    assert _fused(n=n, p=p, k=k, grads=g, workspace=ws + 8, workspace_bytes=4096) == \
+        z.ZS_ERR_CAPACITY                                                      # misaligned
+    assert _fused(n=n, p=p, k=k, grads=g, workspace=FAKE + 16, workspace_bytes=4096) == \
+        z.ZS_ERR_ALIAS                                                         # inside w
+    assert _fused(n=n, p=p, k=k, grads=g, workspace=g[3] + 2 * 7 * 196 + 8,
+                  workspace_bytes=4096) == z.ZS_ERR_ALIAS                      # on a gradient
+    # every check passed: the launch itself fails on a host without a device
+    assert _fused(n=n, p=p, k=k, grads=g, workspace=ws, workspace_bytes=4096) == z.ZS_ERR_HIP
+    # 256 ranks still travel as kernel arguments: no workspace needed
+    g256 = g[:256]
+    assert _fused(n=n, p=256, k=7, grads=g256) == z.ZS_ERR_HIP
+
+
+@no_device
+def test_mean_many_ranks_and_16bit_output_errors():
+    n, p = 100_000, 1024
+    g = [FAKE + (8 << 30) + (r << 24) for r in range(p)]
+    out = FAKE + (1 << 20)
+    f = z.zs_reduce_scatter_mean_local
+    assert f(g, n, p, 3, out, grad_dtype="f16", check=False) == z.ZS_ERR_HIP   # passes of 256
+    assert f(g + [FAKE], n, 1025, 3, out, grad_dtype="f16", check=False) == z.ZS_ERR_ARG
+    f16 = z.zs_reduce_scatter_mean_local16
+    g4 = g[:4]
+    assert f16(g4, n, 4, 1, out, "bf16", grad_dtype="f16", check=False) == z.ZS_ERR_HIP
+    assert f16(g4, n, 4, 1, out, 0, grad_dtype="f16", check=False) == z.ZS_ERR_DTYPE
+    assert f16(g4, n, 4, 1, out, 3, grad_dtype="f16", check=False) == z.ZS_ERR_DTYPE
+    assert f16(g4, n, 4, 1, None, "f16", grad_dtype="f16", check=False) == z.ZS_ERR_NULL
+    # a 16-bit output of 25,000 elements is 50,000 bytes: one byte pair onto rank 2's slice
+    assert f16(g4, n, 4, 1, g4[2] + 2 * 25_000 - 50_000 + 2, "f16", grad_dtype="f16",
+               check=False) == z.ZS_ERR_ALIAS
+    # more than 256 ranks: the fp32 sums between passes need `partial`
+    assert f16(g, n, p, 3, out, "f16", grad_dtype="f16", check=False) == z.ZS_ERR_NULL
+    part = FAKE + (2 << 30)
+    assert f16(g, n, p, 3, out, "f16", grad_dtype="f16", partial=part,
+               check=False) == z.ZS_ERR_HIP
+    assert f16(g, n, p, 3, out, "f16", grad_dtype="f16", partial=out + 64,
+               check=False) == z.ZS_ERR_ALIAS
+
+
+def test_chunk_rule():
+    whole = 28 * 256 * 8
+    # two whole chunks per CU or more: the kernel's whole chunk
+    assert z.zs_mt_chunk_elems(2 * whole * 256, 1, 256) == whole
+    assert z.zs_mt_chunk_elems(1_003_782_656, 42, 256) == whole            # Llama-3-8B shard 3
+    # less: the per-CU share (a quarter with several pieces), up to 2,048
+    assert z.zs_mt_chunk_elems(15_554_976, 1, 256) == 61_440               # GPT-2 shard 0
+    assert z.zs_mt_chunk_elems(15_554_976, 35, 256) == 16_384              # GPT-2 shard 7
+    assert z.zs_mt_chunk_elems(2 * whole * 256 - 1, 1, 256) == 2 * whole  # one chunk per CU
+    assert z.zs_mt_chunk_elems(1, 1, 256) == 2048
+    assert z.zs_mt_chunk_elems(0, 1, 256) == 2048
+    assert z.zs_mt_chunk_elems(10_000_000, 1, 80) == whole
+    assert z.zs_mt_chunk_elems(-1, 1, 256) == 0
+    assert z.zs_mt_chunk_elems(100, 0, 256) == 0
+    for L in (3, 999, 123_457, 9_999_999):
+        for npc in (1, 2, 40):
+            c = z.zs_mt_chunk_elems(L, npc, 256)
+            assert c % 2048 == 0 and 2048 <= c <= 2 * whole
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_buckets_are_minimal_runs(seed):
+    rng = np.random.default_rng(seed)
+    lens = [int(x) for x in rng.integers(1, 5000, int(rng.integers(1, 60)))]
+    pieces = [(i, 0, sum(lens[:i]), ln) for i, ln in enumerate(lens)]
+    B = int(rng.integers(1, 20_000))
+    of, nb = z.zs_plan_buckets(pieces, B)
+    assert of[0] == 0 and of == sorted(of) and nb == of[-1] + 1
+    assert all(b - a in (0, 1) for a, b in zip(of, of[1:]))              # consecutive runs
+    for b in range(nb):
+        run = [lens[i] for i in range(len(lens)) if of[i] == b]
+        if b < nb - 1:
+            assert sum(run) >= B and sum(run) - run[-1] < B                # closed at B
+        else:
+            assert sum(run) - run[-1] < B                                  # last may be short
+    assert z.zs_plan_buckets(pieces, 0) == ([0] * len(lens), 1)
+    assert z.zs_plan_buckets(pieces, 1) == (list(range(len(lens))), len(lens))
+    assert z.zs_plan_buckets([], 10) == ([], 0)
+    with pytest.raises(z.ZsError):
+        z.zs_plan_buckets([(0, 0, 0, 0)], 10)
+
+
+def test_step_table_layout_and_errors():
+    assert z.zs_step_table_bytes(0) == 0
+    assert z.zs_step_table_bytes(1) == 256
+    assert z.zs_step_table_bytes(5) == 256                 # 48 + 5 * 36 bytes
+    assert z.zs_step_table_bytes(6) == 512
+    L = z.lib()
+    import ctypes as C
+
+    t = z.zs_step_table()
+    assert L.zs_step_table_init(C.byref(HP), 8, 0, FAKE, 256, None, C.byref(t)) == z.ZS_ERR_ARG
+    assert L.zs_step_table_init(C.byref(HP), 0, 4, FAKE, 256, None, C.byref(t)) == z.ZS_ERR_ARG
+    assert L.zs_step_table_init(C.byref(HP), 1025, 4, FAKE, 256, None, C.byref(t)) == \
+        z.ZS_ERR_ARG
+    assert L.zs_step_table_init(C.byref(HP), 8, 4, None, 256, None, C.byref(t)) == z.ZS_ERR_NULL
+    assert L.zs_step_table_init(C.byref(HP), 8, 4, FAKE + 16, 256, None, C.byref(t)) == \
+        z.ZS_ERR_CAPACITY
+    assert L.zs_step_table_init(C.byref(HP), 8, 4, FAKE, 255, None, C.byref(t)) == \
+        z.ZS_ERR_CAPACITY
+    bad = z.hparams(1e-3, 0.9, 0.999, 1e-8, 0)
+    assert L.zs_step_table_init(C.byref(bad), 8, 4, FAKE, 256, None, C.byref(t)) == z.ZS_ERR_ARG
+    # handles are checked before any launch
+    st = z.zs_step_table(dev=None, first_step=1, nsteps=4, p=8, form=0)
+    assert z.zs_step_table_advance(st, check=False) == z.ZS_ERR_NULL
+    st.dev = FAKE
+    st.nsteps = 0
+    assert z.zs_step_table_advance(st, check=False) == z.ZS_ERR_ARG
+    st.nsteps, st.form = 4, 7
+    assert z.zs_step_table_advance(st, check=False) == z.ZS_ERR_ARG
+    st.form = 0
+    mt = z.zs_mt_table(workspace=FAKE + (1 << 30), nchunks=4, chunk_elems=64, npieces=1, p=4,
+                       grad_dtype=1, param_dtype=1, state=3)
+    assert z.zs_fused_shard_step_multi_dev(mt, st, check=False) == z.ZS_ERR_ARG   # p differs
+    st.form = 1
+    mt.state = 1
+    mt.p = 8
+    assert z.zs_fused_shard_step_multi_dev(mt, st, check=False) == z.ZS_ERR_NULL  # no v
+
+
+@no_device
+def test_step_table_calls_reach_the_device():
+    st = z.zs_step_table(dev=FAKE, first_step=1, nsteps=4, p=8, form=0)
+    assert z.zs_step_table_advance(st, check=False) == z.ZS_ERR_HIP
+    mt = z.zs_mt_table(workspace=FAKE + (1 << 30), nchunks=4, chunk_elems=64, npieces=1, p=8,
+                       grad_dtype=1, param_dtype=1, state=3)
+    assert z.zs_fused_shard_step_multi_dev(mt, st, check=False) == z.ZS_ERR_HIP
+
+
+@no_device
+def test_offload_argument_errors():
+    import numpy as np
+
+    n, p, k = 1000, 4, 1                      # shard [250, 500): 250 elements
+    g = [FAKE + (8 << 30) + (r << 24) for r in range(p)]
+    host = [np.zeros(250, np.float32) for _ in range(3)]
+    g16 = [np.zeros(250, np.uint16) for _ in range(2)]
+    ph = np.zeros(250, np.uint16)
+    hp = HP
+
+    def off(mode=z.ZS_OFFLOAD_PLAIN, slot=0, p=p, k=k, grads=g, g16_dev=FAKE, param=FAKE + (1 << 30),
+            w=host[0], m=host[1], v=host[2], g16_host=g16, bucket=0, partial=None, hp=hp):
+        return z.zs_offload_step(n, p, k, grads, param, g16_dev, g16_host, w, m, v, ph, hp, mode,
+                                 slot, grad_dtype="f16", param_dtype="f16", partial=partial,
+                                 bucket_elems=bucket, check=False)
+
+    assert off(mode=3) == z.ZS_ERR_ARG
+    assert off(slot=2) == z.ZS_ERR_ARG
+    assert off(k=4) == z.ZS_ERR_ARG
+    assert off(bucket=-1) == z.ZS_ERR_ARG
+    assert off(bucket=0) == z.ZS_ERR_HIP                     # every check passed
+    assert off(hp=z.hparams(1e-3, 0.9, 0.999, 1e-8, 0)) == z.ZS_ERR_ARG
+    assert off(g16_dev=None) == z.ZS_ERR_NULL
+    assert off(w=None) == z.ZS_ERR_NULL
+    assert off(mode=z.ZS_OFFLOAD_RECEIVE, w=None, m=None, v=None) == z.ZS_ERR_HIP  # no update
+    assert off(mode=z.ZS_OFFLOAD_DELAYED, g16_host=[g16[0], None]) == z.ZS_ERR_NULL
+    # host buffers overlapping: m inside w
+    assert off(m=host[0][10:]) == z.ZS_ERR_ALIAS
+    # the gradient being received overlaps the one being applied
+    assert off(mode=z.ZS_OFFLOAD_DELAYED, g16_host=[g16[0], g16[0][5:]]) == z.ZS_ERR_ALIAS
+    # device: the rounded mean on top of rank 2's slice
+    assert off(g16_dev=g[2] + 2 * 250 + 64) == z.ZS_ERR_ALIAS
+    # more than 256 ranks need the fp32 partial sums
+    g300 = [FAKE + (8 << 30) + (r << 24) for r in range(300)]
+    assert off(p=300, k=0, grads=g300) == z.ZS_ERR_NULL
+    assert off(p=300, k=0, grads=g300, partial=FAKE + (2 << 30)) == z.ZS_ERR_HIP
+    assert off(bucket=1) == z.ZS_ERR_HIP                     # 250 buckets of one element

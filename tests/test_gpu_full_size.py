@@ -1,5 +1,6 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
-bench times (one call per shard and step, as bench.py makes it).
+bench times (one call per shard and step, and for the chunk table the chunk
+length zs_mt_chunk_elems gives, as bench.py makes them).
 
 The step is elementwise once the shard map is fixed, so the oracle runs on
 the gathered inputs of a sample of elements (random positions plus every
@@ -109,14 +110,22 @@ def test_zero_7p5b_p64_shard63_five_steps():
     assert torch.equal(param[s[k] // 2:s[k] // 2 + 4096].view(torch.int16), sent)
 
 
-def test_llama3_8b_p8_shard3_multi_tensor_five_steps():
+@pytest.mark.parametrize("chunk_rule", ["bench", "1Mi"])
+def test_llama3_8b_p8_shard3_multi_tensor_five_steps(chunk_rule):
+    # "bench": the chunk length bench.py times (zs_mt_chunk_elems: the kernel's
+    # whole chunk, 57,344 elements, one whole chunk per table entry)
     wl = WORKLOADS["llama3_8b_p8"]
     k = wl.shards[0]
     numel = [n for _, n in wl.tensors]
     assert sum(numel) == wl.n
     M, s, e = oracle.plan_shards(wl.n, wl.p)
     L = e[k] - s[k]
-    chunk = 1 << 20
+    if chunk_rule == "bench":
+        npieces = len(z.zs_plan_chunks(numel, wl.p, k, 8)[0])
+        chunk = z.zs_mt_chunk_elems(L, npieces)
+        assert chunk == 28 * 256 * 8
+    else:
+        chunk = 1 << 20
     pieces, nchunks = z.zs_plan_chunks(numel, wl.p, k, chunk)
     ref_pieces = oracle.shard_pieces(numel, s[k], e[k])
     assert pieces == ref_pieces and len(pieces) == 42

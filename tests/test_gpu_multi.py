@@ -118,23 +118,47 @@ def test_random_tensor_lists_all_shards(seed):
         _run_and_check(case, 2, seed_for(41, seed, k))
 
 
-def test_gpt2_small_shapes_shard0_ten_steps():
+def _bench_chunk(numel, p, k):
+    """The chunk length bench.py uses for rank k's shard (zs_mt_chunk_elems)."""
+    M, s, e = oracle.plan_shards(sum(numel), p)
+    npieces = len(z.zs_plan_chunks(numel, p, k, 8)[0])
+    return z.zs_mt_chunk_elems(e[k] - s[k], npieces)
+
+
+@pytest.mark.parametrize("chunk_rule", ["bench", "65536"])
+def test_gpt2_small_shapes_shard0_ten_steps(chunk_rule):
     wl = WORKLOADS["gpt2_small_p8"]
     numel = [n for _, n in wl.tensors]
-    case = MtCase(numel, wl.p, 0, wl.grad_dtype, wl.param_dtype, 65536, 42)
+    chunk = _bench_chunk(numel, wl.p, 0) if chunk_rule == "bench" else 65536
+    if chunk_rule == "bench":
+        ncu = torch.cuda.get_device_properties(0).multi_processor_count
+        assert ncu != 256 or chunk == 61_440
+    case = MtCase(numel, wl.p, 0, wl.grad_dtype, wl.param_dtype, chunk, 42)
     assert len(case.pieces) == 1
-    say("gpt2 shard 0: 10 steps")
+    say(f"gpt2 shard 0: 10 steps, chunk {chunk}")
     _run_and_check(case, wl.steps, 43, check_every=False)
 
 
+@pytest.mark.parametrize("chunk_rule", ["bench", "65536"])
 @pytest.mark.parametrize("k", [2, 7])
-def test_gpt2_small_shapes_many_pieces(k):
+def test_gpt2_small_shapes_many_pieces(k, chunk_rule):
     wl = WORKLOADS["gpt2_small_p8"]
     numel = [n for _, n in wl.tensors]
-    case = MtCase(numel, wl.p, k, wl.grad_dtype, wl.param_dtype, 65536, 44 + k)
+    chunk = _bench_chunk(numel, wl.p, k) if chunk_rule == "bench" else 65536
+    case = MtCase(numel, wl.p, k, wl.grad_dtype, wl.param_dtype, chunk, 44 + k)
     assert len(case.pieces) in (15, 35)
-    say(f"gpt2 shard {k}: {len(case.pieces)} pieces, 2 steps")
+    say(f"gpt2 shard {k}: {len(case.pieces)} pieces, chunk {chunk}, 2 steps")
     _run_and_check(case, 2, 46 + k)
+
+
+def test_table_at_1024_ranks():
+    # the chunk table stages up to ZS_MAX_P gradient pointers per entry in LDS
+    numel = [30_011, 7, 52_001]
+    p, k = 1024, 370           # M = 81: the shard crosses all three tensors
+    case = MtCase(numel, p, k, "bf16", "bf16", 2048, 50)
+    assert [pc[3] for pc in case.pieces] == [41, 7, 33]
+    say(f"1024 ranks: shard {k}, pieces {[pc[3] for pc in case.pieces]}")
+    _run_and_check(case, 2, 51)
 
 
 def test_multi_equals_single_tensor_step():
