@@ -15,6 +15,7 @@
 
 static_assert(ZS_MAX_P == zs::kMaxP, "ZS_MAX_P and the kernel table size must agree");
 static_assert(ZS_KERNARG_P == zs::kKernargP, "ZS_KERNARG_P and the kernel arguments must agree");
+static_assert(ZS_STATIC_SCRATCH_BYTES == zs::kStaticScratchBytes, "static scratch size");
 static_assert(sizeof(zs::StepTableDev) <= zs::kStepTableHead, "step table layout");
 
 namespace {
@@ -133,7 +134,13 @@ zs_status zs_plan_shards(int64_t n, int32_t p, int64_t* m_out, int64_t* starts, 
 
 size_t zs_shard_workspace_bytes(int32_t p) { return rank_table_bytes(p); }
 
-zs_status zs_fused_shard_step(const zs_shard_args* a) {
+}  // extern "C"
+
+namespace {
+
+// The fused step; the rank pointer table of p > ZS_KERNARG_P ranks goes to
+// the caller's workspace, or (use_static) to the library's static scratch.
+zs_status fused_impl(const zs_shard_args* a, bool use_static) {
   if (!a) return ZS_ERR_NULL;
   if (a->p < 1 || a->p > ZS_MAX_P || a->k < 0 || a->k >= a->p || a->n < 0) return ZS_ERR_ARG;
   if (a->n > kMaxN) return ZS_ERR_RANGE;
@@ -198,15 +205,23 @@ zs_status zs_fused_shard_step(const zs_shard_args* a) {
   L.rank_table = nullptr;
   if (a->p > ZS_KERNARG_P) {
     const size_t need = rank_table_bytes(a->p);
-    const uintptr_t pw_ = reinterpret_cast<uintptr_t>(a->workspace);
-    if (!a->workspace || a->workspace_bytes < need || pw_ % 16u != 0) return ZS_ERR_CAPACITY;
-    const Range wsr{pw_, pw_ + need};
-    for (const Range& wr : writes)
-      if (overlap(wsr, wr)) return ZS_ERR_ALIAS;
-    for (const Range& rd : reads)
-      if (overlap(wsr, rd)) return ZS_ERR_ALIAS;
-    L.rank_table = static_cast<const uint16_t* const*>(a->workspace);
-    const hipError_t e = fill_rank_table(L.grads, a->p, a->workspace, L.stream);
+    void* table = nullptr;
+    if (use_static) {
+      if (need > zs::kStaticScratchBytes) return ZS_ERR_CAPACITY;
+      const hipError_t e = zs::static_scratch(&table);
+      if (e != hipSuccess) return hip_fail(e);
+    } else {
+      const uintptr_t pw_ = reinterpret_cast<uintptr_t>(a->workspace);
+      if (!a->workspace || a->workspace_bytes < need || pw_ % 16u != 0) return ZS_ERR_CAPACITY;
+      const Range wsr{pw_, pw_ + need};
+      for (const Range& wr : writes)
+        if (overlap(wsr, wr)) return ZS_ERR_ALIAS;
+      for (const Range& rd : reads)
+        if (overlap(wsr, rd)) return ZS_ERR_ALIAS;
+      table = a->workspace;
+    }
+    L.rank_table = static_cast<const uint16_t* const*>(table);
+    const hipError_t e = fill_rank_table(L.grads, a->p, table, L.stream);
     if (e != hipSuccess) return hip_fail(e);
   }
 
@@ -214,6 +229,14 @@ zs_status zs_fused_shard_step(const zs_shard_args* a) {
   if (err != hipSuccess) return hip_fail(err);
   return ZS_OK;
 }
+
+}  // namespace
+
+extern "C" {
+
+zs_status zs_fused_shard_step(const zs_shard_args* a) { return fused_impl(a, false); }
+
+zs_status zs_fused_shard_step_static(const zs_shard_args* a) { return fused_impl(a, true); }
 
 }  // extern "C"
 

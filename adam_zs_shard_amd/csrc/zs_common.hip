@@ -2,8 +2,21 @@
 
 #include "zs_device.h"
 
+#include <mutex>
+
 namespace zs {
+
+// The allocation-free fused step's scratch: the rank pointer table, written
+// by rank_table_kernel and read by the step's kernels.  Each GPU holds its own
+// copy for the life of the process.  Host code must not use this name as an
+// address (in host code it is a stand-in, not device memory): it takes the
+// address from static_scratch() below.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
 namespace {
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};   // per device, guarded by g_scratch_mu
 
 // Copies the n <= kKernargP rank pointers of this launch's kernel arguments
 // into a device array, one pointer per lane.  The pointers are read through
@@ -37,6 +50,23 @@ int cu_count() {
     n = 256;
   if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
   return n;
+}
+
+hipError_t static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    // once per device, with that device current: its own copy's address
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_rank_table(const uint16_t* const* src, int n, const uint16_t** dst,

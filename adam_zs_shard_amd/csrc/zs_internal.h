@@ -151,6 +151,13 @@ hipError_t launch_step_advance(StepTableDev* t, hipStream_t stream);
 // groups on 16-byte boundaries.
 int choose_head(const std::vector<uintptr_t>& a16, const std::vector<uintptr_t>& a32);
 
+// Bytes of the library's static device scratch (one copy per GPU): the rank
+// pointer table of up to kMaxP ranks for the allocation-free fused step.
+constexpr size_t kStaticScratchBytes = static_cast<size_t>(kMaxP) * sizeof(void*);
+// Device address of the current device's static scratch, looked up once per
+// device with that device current (hipGetSymbolAddress) and cached.
+hipError_t static_scratch(void** out);
+
 // Records e as this thread's last HIP error (zs_last_hip_error) and returns
 // ZS_ERR_HIP.
 int32_t hip_status(hipError_t e);

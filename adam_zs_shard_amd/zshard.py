@@ -21,6 +21,7 @@ ZS_ADAM_STANDARD, ZS_ADAM_PAGE1_LITERAL, ZS_SGD, ZS_SGD_MOMENTUM = 0, 1, 2, 3
 ZS_STATE_M, ZS_STATE_V = 1, 2
 ZS_MAX_P = 1024
 ZS_KERNARG_P = 256
+ZS_STATIC_SCRATCH_BYTES = 8192
 
 FORMS = {"standard": ZS_ADAM_STANDARD, "page1_literal": ZS_ADAM_PAGE1_LITERAL, "sgd": ZS_SGD,
          "sgd_momentum": ZS_SGD_MOMENTUM}
@@ -92,7 +93,8 @@ class zs_step_table(C.Structure):
 
 EXPORTS = [
     "zs_status_string", "zs_version", "zs_last_hip_error", "zs_plan_shards",
-    "zs_shard_workspace_bytes", "zs_fused_shard_step", "zs_reduce_scatter_mean_local",
+    "zs_shard_workspace_bytes", "zs_fused_shard_step", "zs_fused_shard_step_static",
+    "zs_reduce_scatter_mean_local",
     "zs_reduce_scatter_mean_local16", "zs_adam_step", "zs_plan_chunks", "zs_mt_chunk_elems",
     "zs_plan_buckets", "zs_mt_workspace_bytes", "zs_mt_upload", "zs_fused_shard_step_multi",
     "zs_step_table_bytes", "zs_step_table_init", "zs_step_table_advance", "zs_step_table_status",
@@ -122,6 +124,8 @@ def lib():
         L.zs_shard_workspace_bytes.restype = C.c_size_t
         L.zs_fused_shard_step.argtypes = [C.POINTER(zs_shard_args)]
         L.zs_fused_shard_step.restype = i32
+        L.zs_fused_shard_step_static.argtypes = [C.POINTER(zs_shard_args)]
+        L.zs_fused_shard_step_static.restype = i32
         L.zs_reduce_scatter_mean_local.argtypes = [C.POINTER(vp), i32, i64, i64, i32, i32, vp, vp]
         L.zs_reduce_scatter_mean_local.restype = i32
         L.zs_reduce_scatter_mean_local16.argtypes = [C.POINTER(vp), i32, i64, i64, i32, i32, vp,
@@ -245,9 +249,12 @@ def zs_shard_workspace_bytes(p: int) -> int:
 
 def zs_fused_shard_step(n, p, k, grads, w, m, v, param, hp: zs_adam_hparams, *,
                         grad_base=0, param_base=0, grad_dtype=None, param_dtype=None,
-                        stream=None, workspace=None, workspace_bytes=None, check=True) -> int:
+                        stream=None, workspace=None, workspace_bytes=None, static=False,
+                        check=True) -> int:
     """workspace: device memory for the rank pointer table (needed when p >
-    ZS_KERNARG_P); workspace_bytes defaults to the tensor's size in bytes."""
+    ZS_KERNARG_P); workspace_bytes defaults to the tensor's size in bytes.
+    static=True calls zs_fused_shard_step_static (no workspace: the library's
+    static device scratch)."""
     gptr, keep = _ptr_array(grads)
     if workspace_bytes is None:
         workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else \
@@ -259,10 +266,11 @@ def zs_fused_shard_step(n, p, k, grads, w, m, v, param, hp: zs_adam_hparams, *,
         grad_base=grad_base, w=_addr(w), m=_addr(m), v=_addr(v), param=_addr(param),
         param_base=param_base, hp=C.pointer(hp), stream=_stream(stream),
         workspace=_addr(workspace), workspace_bytes=workspace_bytes)
-    st = lib().zs_fused_shard_step(C.byref(a))
+    fn = lib().zs_fused_shard_step_static if static else lib().zs_fused_shard_step
+    st = fn(C.byref(a))
     del keep
     if check:
-        _check(st, "zs_fused_shard_step")
+        _check(st, "zs_fused_shard_step_static" if static else "zs_fused_shard_step")
     return st
 
 

@@ -171,6 +171,20 @@ size_t zs_shard_workspace_bytes(int32_t p);
  * aligned), ZS_ERR_HIP. */
 zs_status zs_fused_shard_step(const zs_shard_args* args);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * step as zs_fused_shard_step, bit for bit, with the rank pointer table of p
+ * > ZS_KERNARG_P ranks kept in a static device array of the library
+ * (ZS_STATIC_SCRATCH_BYTES per GPU, held until the process ends) instead of
+ * args->workspace, which is ignored.  Allocates nothing: no hipMalloc, no
+ * hipFree, no allocating library call.  Every call on one GPU shares that
+ * GPU's array, so calls that overlap on one GPU (on different streams) race
+ * and must not be issued; calls on one stream are ordered and safe.  For p <=
+ * ZS_KERNARG_P it uses no scratch at all.  Errors: as zs_fused_shard_step,
+ * ZS_ERR_CAPACITY if the table would exceed the array. */
+#define ZS_STATIC_SCRATCH_BYTES 8192 /* ZS_MAX_P rank pointers */
+zs_status zs_fused_shard_step_static(const zs_shard_args* args);
+
 /* The gradient mean alone, stored (the local stand-in for reduce-scatter +
  * mean; [DP-III] §(四) step 2 keeps the slice mean in memory before the
  * moment update): g_out[i] = mean over ranks of global

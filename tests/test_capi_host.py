@@ -34,7 +34,7 @@ def _declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert len(names) == 22 and sorted(names) == sorted(z.EXPORTS)
+    assert len(names) == 23 and sorted(names) == sorted(z.EXPORTS)
     L = z.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -466,3 +466,20 @@ def test_offload_argument_errors():
     assert off(p=300, k=0, grads=g300) == z.ZS_ERR_NULL
     assert off(p=300, k=0, grads=g300, partial=FAKE + (2 << 30)) == z.ZS_ERR_HIP
     assert off(bucket=1) == z.ZS_ERR_HIP                     # 250 buckets of one element
+
+
+@no_device
+def test_static_scratch_entry_checks_like_the_workspace_one():
+    n, p, k = 100_000, 512, 7
+    g = [FAKE + (8 << 30) + (r << 24) for r in range(p)]
+
+    def st(**kw):
+        return z.zs_fused_shard_step(n, p, k, g, FAKE, FAKE + (1 << 30), FAKE + (2 << 30),
+                                     FAKE + (3 << 30), kw.pop("hp", HP), grad_dtype="f16",
+                                     param_dtype="f16", static=True, check=False, **kw)
+
+    assert st() == z.ZS_ERR_HIP                              # no workspace needed
+    assert st(hp=z.hparams(1e-3, 0.9, 0.999, 1e-8, 0)) == z.ZS_ERR_ARG
+    assert z.zs_fused_shard_step(n, 1025, k, g + g[:513], FAKE, FAKE + (1 << 30),
+                                 FAKE + (2 << 30), FAKE + (3 << 30), HP, grad_dtype="f16",
+                                 param_dtype="f16", static=True, check=False) == z.ZS_ERR_ARG
