@@ -4,27 +4,33 @@
 // gradients and the fp32 (w, m, v), writes (w, m, v) and one 16-bit working
 // copy, and does O(P) flops.  At about 0.5 flop/byte it sits far below the
 // fp32 vector ridge of the chip: the design goal is HBM bandwidth.
-//  - Each lane owns groups of 8 consecutive elements: one 16-byte load per
-//    gradient rank, two per fp32 state array, one 16-byte store of the
-//    16-bit copy.  Addresses are a workgroup-uniform base (SGPRs) plus a
-//    fixed per-lane byte offset, so a wave64 access is 1 KiB contiguous.
-//  - Gradient reads are rank-major: for each rank in turn a wave issues one
-//    load (group 0), uses it, then the other 27 loads of the chunk back to
-//    back (scheduling barriers stop the compiler from sinking each load next
-//    to its use), then adds them into the per-group sums.  Every element receives the ranks in order 0..P-1: a
-//    left fold, one fp32 rounding per add, exactly the oracle's order.
-//    All loads and stores are non-temporal (each byte is touched once).
+//  - Work comes in groups of 2048 elements, 8 per lane of a 256-lane
+//    workgroup, at a workgroup-uniform base (SGPRs) plus per-lane byte
+//    offsets.  In a full group, lane l of wave wv owns two quads: elements
+//    512 wv + 4l + {0..3} and 512 wv + 256 + 4l + {0..3} of the group (the
+//    lane map, Lanes below).  Every access is then a whole-line stream: each
+//    8-byte access of a 16-bit array (gradients, working copy) covers 512
+//    contiguous bytes per wave, each 16-byte access of an fp32 array (w, m,
+//    v) 1 KiB, so no store instruction leaves a cache line half written.  The
+//    last, partial group of a range keeps 8 consecutive elements per lane.
+//  - Gradient reads are rank-major: for each rank in turn a wave issues its
+//    first group's loads, uses them, then the other 27 groups' loads of the
+//    chunk back to back (scheduling barriers stop the compiler from sinking
+//    each load next to its use), then adds them into the per-group sums.
+//    Every element receives the ranks in order 0..P-1: a left fold, one fp32
+//    rounding per add, exactly the oracle's order.  All loads and stores are
+//    non-temporal (each byte is touched once).
 //  - Phase separation: HBM on this part streams reads alone far faster than
 //    reads with any writes mixed in.  A workgroup therefore sums the
-//    gradients of a whole chunk (up to 28 groups per lane, held in registers
-//    with one wave per SIMD) before it touches w, m, v and the working copy,
-//    so reads and writes reach the memory in separate stretches.
-//  - One workgroup per CU.  Full chunks (28 groups per lane) go round-robin;
-//    the remainder (at most one chunk's worth, plus up to 14 scalar
-//    elements) is dealt to the workgroups that got one chunk fewer, and is
-//    read with the ranks batched, so the workgroups finish together.
-//    Shards under half a chunk per CU get no whole chunk: small_kernel deals
-//    their pieces over four workgroups per CU instead.
+//    gradients of a whole chunk (28 groups, held in registers with one wave
+//    per SIMD) before it touches w, m, v and the working copy, so reads and
+//    writes reach the memory in separate stretches.
+//  - One workgroup per CU.  Full chunks (28 groups) go round-robin; the
+//    remainder (at most one chunk's worth, plus up to 14 scalar elements) is
+//    dealt to the workgroups that got one chunk fewer, and is read with the
+//    ranks batched, so the workgroups finish together.  Shards under half a
+//    chunk per CU get no whole chunk: small_kernel deals their pieces over
+//    four workgroups per CU instead.
 //  - No MFMA and no LDS on the single-tensor path (nothing is reused); the
 //    multi-tensor path stages one chunk's descriptors in LDS.
 // Arithmetic (rank-order fp32 mean, Adam moments, bias correction, update,
@@ -34,7 +40,6 @@
 // Compiled with -ffp-contract=off and the pragma below: no FMA contraction;
 // division and sqrt are the correctly rounded HIP defaults; fp32 denormals
 // are kept.
-
 
 #pragma once
 
@@ -50,26 +55,27 @@
 namespace zs {
 namespace {
 
-// 16-byte vectors that may sit at any 2-byte (u16) or 4-byte (fp32) address:
-// gfx950 runs with unaligned access enabled, so these still compile to
-// global_load_dwordx4 / global_store_dwordx4.
+// Vectors that may sit at any 2-byte (u16) or 4-byte (fp32) address: gfx950
+// runs with unaligned access enabled, so these still compile to single
+// global_load / global_store instructions of 8 or 16 bytes.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4), aligned(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2), aligned(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4), aligned(4)));
 
-// Groups of 8 elements per lane whose rank sums are held in registers across
-// the read-only phase of a full chunk (28 x 8 fp32 values per lane: with one
-// wave per SIMD the kernel may use the whole 512-entry register file), the
-// gradient loads a wave issues back to back, and the groups of the smaller
-// chunks that take the remainder of a range.
+// Groups whose rank sums are held in registers across the read-only phase of
+// a full chunk (28 x 8 fp32 values per lane: with one wave per SIMD the
+// kernel may use the whole 512-entry register file), the gradient loads a
+// wave issues back to back, and the groups of the smaller chunks that take
+// the remainder of a range.
 constexpr int kGroupsMax = 28;
-// Gradient loads per batch of a rank in the whole-chunk read phase (after
-// the probe load of group 0): fused_kernel issues the rest of the chunk, 27
-// loads, in one batch (1.7% faster at 64 ranks than two batches of 14);
-// table_kernel keeps batches of 14 (0.5% faster at 8 ranks).
+// Groups of loads per batch of a rank in the whole-chunk read phase (after
+// the probe loads of group 0): fused_kernel issues the rest of the chunk, 27
+// groups, in one batch; table_kernel keeps batches of 14.
 constexpr int kLoadBatch = 28;
 constexpr int kTableLoadBatch = 14;
 static_assert(kGroupsMax % kLoadBatch == 0, "whole load batches per chunk");
 static_assert(kGroupsMax % kTableLoadBatch == 0, "whole load batches per chunk");
+constexpr int64_t kGroup = static_cast<int64_t>(kBlock) * kVec;  // elements per group
 
 template <int DT>
 __device__ __forceinline__ float widen_lo(uint32_t x) {
@@ -195,8 +201,33 @@ constexpr int kRankBatch = 8;
 // Waves per SIMD (workgroups per CU) of the small-shard kernel.
 constexpr int kSmallWaves = 4;
 
-// 16-byte loads at a workgroup-uniform base plus a per-lane byte offset; the
-// gradient loads are non-temporal (each byte is read once per step).
+// ---- the lane maps -------------------------------------------------------
+// Byte offsets of one lane inside a group, added to a workgroup-uniform base
+// at the group's first element.  Full groups: quad A of 16-bit arrays at
+// q16 (quad B at q16 + 512), of fp32 arrays at q32 (quad B at q32 + 1024).
+// The partial group: 8 consecutive elements at c16 / c32.
+struct Lanes {
+  uint32_t q16, q32, c16, c32;
+};
+
+__device__ __forceinline__ Lanes lanes() {
+  const uint32_t wv = threadIdx.x >> 6, l = threadIdx.x & 63u;
+  const uint32_t q = wv * 512u + 4u * l;
+  return Lanes{2u * q, 4u * q, 16u * threadIdx.x, 32u * threadIdx.x};
+}
+
+// The 8 gradients of a lane in a full group: quads A and B.
+struct G8 {
+  u32x2 a, b;
+};
+
+// Non-temporal loads (each byte is read once per step; plain gradient loads
+// cost 10% on the 7.5B-parameter, 64-rank shard).
+__device__ __forceinline__ G8 ld_g8(const uint16_t* base, const Lanes& L) {
+  const char* p = reinterpret_cast<const char*>(base);
+  return G8{__builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p + L.q16)),
+            __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p + L.q16 + 512u))};
+}
 __device__ __forceinline__ u32x4 ld_grad(const uint16_t* base, uint32_t off) {
   return __builtin_nontemporal_load(
       reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + off));
@@ -206,14 +237,31 @@ __device__ __forceinline__ f32x4 ld_f32x4(const float* base, uint32_t off) {
       reinterpret_cast<const f32x4*>(reinterpret_cast<const char*>(base) + off));
 }
 // The fp32 state loads and all stores are non-temporal too: each byte of w,
-// m, v and the working copy is read once and written once per step.  Against
-// plain loads and stores this is about 1.4% faster on the 7.5B-parameter,
-// 64-rank shard; plain gradient loads instead of non-temporal ones cost 10%.
+// m, v and the working copy is read once and written once per step.
 __device__ __forceinline__ void st_f32x4(float* base, uint32_t off, f32x4 x) {
   __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(reinterpret_cast<char*>(base) + off));
 }
 __device__ __forceinline__ void st_u16x8(uint16_t* base, uint32_t off, u32x4 x) {
   __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(reinterpret_cast<char*>(base) + off));
+}
+__device__ __forceinline__ void st_u16x4(uint16_t* base, uint32_t off, u32x2 x) {
+  __builtin_nontemporal_store(x, reinterpret_cast<u32x2*>(reinterpret_cast<char*>(base) + off));
+}
+
+// The 8 fp32 values of a lane (quad A then quad B), loaded / stored.
+__device__ __forceinline__ void ld_f8(const float* base, const Lanes& L, float (&x)[kVec]) {
+  const f32x4 a = ld_f32x4(base, L.q32), b = ld_f32x4(base, L.q32 + 1024u);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+__device__ __forceinline__ void st_f8(float* base, const Lanes& L, const float (&x)[kVec]) {
+  st_f32x4(base, L.q32, f32x4{x[0], x[1], x[2], x[3]});
+  st_f32x4(base, L.q32 + 1024u, f32x4{x[4], x[5], x[6], x[7]});
+}
+template <int DT>
+__device__ __forceinline__ void st_h8(uint16_t* base, const Lanes& L, const float (&x)[kVec]) {
+  st_u16x4(base, L.q16, u32x2{narrow2<DT>(x[0], x[1]), narrow2<DT>(x[2], x[3])});
+  st_u16x4(base, L.q16 + 512u, u32x2{narrow2<DT>(x[4], x[5]), narrow2<DT>(x[6], x[7])});
 }
 
 // Which optimizer state a form reads and writes: Adam both moments, momentum
@@ -248,6 +296,46 @@ __device__ __forceinline__ void st_state1(float* p, float x) {
   if constexpr (USE) *p = x;
 }
 
+// ---- gradient folds --------------------------------------------------------
+// Full groups (G8): acc[0..3] from quad A, acc[4..7] from quad B.
+template <int GDT>
+__device__ __forceinline__ void init8(float (&acc)[kVec], const G8& q) {
+  acc[0] = widen_lo<GDT>(q.a.x); acc[1] = widen_hi<GDT>(q.a.x);
+  acc[2] = widen_lo<GDT>(q.a.y); acc[3] = widen_hi<GDT>(q.a.y);
+  acc[4] = widen_lo<GDT>(q.b.x); acc[5] = widen_hi<GDT>(q.b.x);
+  acc[6] = widen_lo<GDT>(q.b.y); acc[7] = widen_hi<GDT>(q.b.y);
+}
+template <int GDT>
+__device__ __forceinline__ void fold8(float (&acc)[kVec], const G8& q) {
+  acc[0] = acc[0] + widen_lo<GDT>(q.a.x); acc[1] = acc[1] + widen_hi<GDT>(q.a.x);
+  acc[2] = acc[2] + widen_lo<GDT>(q.a.y); acc[3] = acc[3] + widen_hi<GDT>(q.a.y);
+  acc[4] = acc[4] + widen_lo<GDT>(q.b.x); acc[5] = acc[5] + widen_hi<GDT>(q.b.x);
+  acc[6] = acc[6] + widen_lo<GDT>(q.b.y); acc[7] = acc[7] + widen_hi<GDT>(q.b.y);
+}
+// One quad (4 consecutive 16-bit values) into acc[j0 .. j0+3].
+__device__ __forceinline__ u32x2 ld_quad(const uint16_t* base, uint32_t off) {
+  return __builtin_nontemporal_load(
+      reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(base) + off));
+}
+template <int GDT>
+__device__ __forceinline__ void init4(float (&acc)[kVec], int j0, const u32x2& q) {
+  acc[j0] = widen_lo<GDT>(q.x); acc[j0 + 1] = widen_hi<GDT>(q.x);
+  acc[j0 + 2] = widen_lo<GDT>(q.y); acc[j0 + 3] = widen_hi<GDT>(q.y);
+}
+template <int GDT>
+__device__ __forceinline__ void fold4(float (&acc)[kVec], int j0, const u32x2& q) {
+  acc[j0] = acc[j0] + widen_lo<GDT>(q.x); acc[j0 + 1] = acc[j0 + 1] + widen_hi<GDT>(q.x);
+  acc[j0 + 2] = acc[j0 + 2] + widen_lo<GDT>(q.y); acc[j0 + 3] = acc[j0 + 3] + widen_hi<GDT>(q.y);
+}
+// The partial group (u32x4): 8 consecutive elements.
+template <int GDT>
+__device__ __forceinline__ void init8(float (&acc)[kVec], const u32x4& q) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    acc[2 * j] = widen_lo<GDT>(q[j]);
+    acc[2 * j + 1] = widen_hi<GDT>(q[j]);
+  }
+}
 template <int GDT>
 __device__ __forceinline__ void fold8(float (&acc)[kVec], const u32x4& q) {
 #pragma unroll
@@ -257,27 +345,34 @@ __device__ __forceinline__ void fold8(float (&acc)[kVec], const u32x4& q) {
   }
 }
 
-template <int GDT>
-__device__ __forceinline__ void init8(float (&acc)[kVec], const u32x4& q) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    acc[2 * j] = widen_lo<GDT>(q[j]);
-    acc[2 * j + 1] = widen_hi<GDT>(q[j]);
+// One lane's gradient vector of a group in either map.
+template <bool FULL>
+using GVec = std::conditional_t<FULL, G8, u32x4>;
+
+template <bool FULL>
+__device__ __forceinline__ GVec<FULL> ld_gvec(const uint16_t* base, const Lanes& L) {
+  if constexpr (FULL) {
+    return ld_g8(base, L);
+  } else {
+    return ld_grad(base, L.c16);
   }
 }
 
-// The loads of ranks r0 .. r0+B-1 for one lane's 8 elements, issued together
-// (the scheduling barriers keep the compiler from sinking each load next to
-// its use, which would leave one load in flight), then added in rank order.
-// CONT: acc already holds the fp32 sums of earlier ranks, so rank r0 = 0 of
-// this call is added to it rather than starting the fold.
-template <int B, int GDT, bool CONT = false, class Grads>
-__device__ __forceinline__ void fold_batch(const Grads& gr, int r0, int64_t e0, uint32_t lane16,
+// The loads of ranks r0 .. r0+B-1 for one lane's 8 elements of the group at
+// e0, issued together (the scheduling barriers keep the compiler from sinking
+// each load next to its use, which would leave one load in flight), then
+// added in rank order.  CONT: acc already holds the fp32 sums of earlier
+// ranks, so rank r0 = 0 of this call is added to it rather than starting the
+// fold.
+template <int B, int GDT, bool FULL, bool CONT = false, class Grads>
+__device__ __forceinline__ void fold_batch(const Grads& gr, int r0, int64_t e0, const Lanes& L,
                                            float (&acc)[kVec]) {
-  u32x4 q[B];
+  GVec<FULL> q[B];
 #pragma unroll
-  for (int b = 0; b < B; ++b) q[b] = ld_grad(gr.get(r0 + b) + e0, lane16);
-  __builtin_amdgcn_sched_barrier(0);
+  for (int b = 0; b < B; ++b) {
+    q[b] = ld_gvec<FULL>(gr.get(r0 + b) + e0, L);
+    __builtin_amdgcn_sched_barrier(0);  // issued in rank order
+  }
   if (!CONT && r0 == 0) {
     init8<GDT>(acc, q[0]);
   } else {
@@ -288,39 +383,46 @@ __device__ __forceinline__ void fold_batch(const Grads& gr, int r0, int64_t e0, 
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// acc[j] = sum over ranks r = 0..p-1, in that order, of widen(grad_r[e0 + 8*lane + j]),
-// in batches of 16 ranks, then one batch each of 8, 4, 2, 1 for the rest: at
-// most 4 + P/16 memory round trips.  e0 is workgroup-uniform, lane16 = 16 * lane.
-template <int GDT, bool CONT = false, class Grads>
-__device__ __forceinline__ void sum_ranks8(const Grads& gr, int p, int64_t e0, uint32_t lane16,
+// acc[j] = sum over ranks r = 0..p-1, in that order, of the lane's element
+// j of the group at e0, in batches of 16 ranks, then one batch each of 8, 4,
+// 2, 1 for the rest: at most 4 + P/16 memory round trips.
+template <int GDT, bool FULL, bool CONT = false, int MAXB = 16, class Grads>
+__device__ __forceinline__ void sum_ranks8(const Grads& gr, int p, int64_t e0, const Lanes& L,
                                            float (&acc)[kVec]) {
   int r0 = 0;
-  for (; r0 + 16 <= p; r0 += 16) fold_batch<16, GDT, CONT>(gr, r0, e0, lane16, acc);
-  if (r0 + 8 <= p) {
-    fold_batch<8, GDT, CONT>(gr, r0, e0, lane16, acc);
-    r0 += 8;
+  if constexpr (MAXB >= 16) {
+    for (; r0 + 16 <= p; r0 += 16) fold_batch<16, GDT, FULL, CONT>(gr, r0, e0, L, acc);
+    if (r0 + 8 <= p) {
+      fold_batch<8, GDT, FULL, CONT>(gr, r0, e0, L, acc);
+      r0 += 8;
+    }
+  } else if constexpr (MAXB == 8) {
+    for (; r0 + 8 <= p; r0 += 8) fold_batch<8, GDT, FULL, CONT>(gr, r0, e0, L, acc);
+  } else {
+    for (; r0 + 4 <= p; r0 += 4) fold_batch<4, GDT, FULL, CONT>(gr, r0, e0, L, acc);
   }
   if (r0 + 4 <= p) {
-    fold_batch<4, GDT, CONT>(gr, r0, e0, lane16, acc);
+    fold_batch<4, GDT, FULL, CONT>(gr, r0, e0, L, acc);
     r0 += 4;
   }
   if (r0 + 2 <= p) {
-    fold_batch<2, GDT, CONT>(gr, r0, e0, lane16, acc);
+    fold_batch<2, GDT, FULL, CONT>(gr, r0, e0, L, acc);
     r0 += 2;
   }
-  if (r0 < p) fold_batch<1, GDT, CONT>(gr, r0, e0, lane16, acc);
+  if (r0 < p) fold_batch<1, GDT, FULL, CONT>(gr, r0, e0, L, acc);
 }
 
-// Two vectors per lane (element offsets e0 and e1): both vectors' loads of
-// ranks r0 .. r0+B-1 in flight together, then the rank-order adds.
-template <int B, int GDT, bool CONT = false, class Grads>
+// Two groups (at e0 and e1, in either map): both groups' loads of ranks
+// r0 .. r0+B-1 in flight together, then the rank-order adds.
+template <int B, int GDT, bool FULL, bool CONT = false, class Grads>
 __device__ __forceinline__ void fold_batch2(const Grads& gr, int r0, int64_t e0, int64_t e1,
-                                            uint32_t lane16, float (&a)[kVec], float (&b)[kVec]) {
-  u32x4 qa[B], qb[B];
+                                            const Lanes& L, float (&a)[kVec], float (&b)[kVec]) {
+  GVec<FULL> qa[B], qb[B];
 #pragma unroll
   for (int i = 0; i < B; ++i) {
-    qa[i] = ld_grad(gr.get(r0 + i) + e0, lane16);
-    qb[i] = ld_grad(gr.get(r0 + i) + e1, lane16);
+    qa[i] = ld_gvec<FULL>(gr.get(r0 + i) + e0, L);
+    qb[i] = ld_gvec<FULL>(gr.get(r0 + i) + e1, L);
+    if constexpr (FULL) __builtin_amdgcn_sched_barrier(0);  // issued in rank order
   }
   __builtin_amdgcn_sched_barrier(0);
   if (!CONT && r0 == 0) {
@@ -338,32 +440,33 @@ __device__ __forceinline__ void fold_batch2(const Grads& gr, int r0, int64_t e0,
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// MAXB caps the rank batch (8 keeps the small-shard kernel within the
-// registers of four waves per SIMD).
-template <int GDT, int MAXB = 16, bool CONT = false, class Grads>
+// MAXB caps the rank batch (16, 8 or 4): the small-shard kernel, with four
+// waves per SIMD, takes 4.
+template <int GDT, int MAXB = 16, bool FULL = true, bool CONT = false, class Grads>
 __device__ __forceinline__ void sum_ranks8x2(const Grads& gr, int p, int64_t e0, int64_t e1,
-                                             uint32_t lane16, float (&a)[kVec],
+                                             const Lanes& L, float (&a)[kVec],
                                              float (&b)[kVec]) {
   int r0 = 0;
   if constexpr (MAXB >= 16) {
-    for (; r0 + 16 <= p; r0 += 16) fold_batch2<16, GDT, CONT>(gr, r0, e0, e1, lane16, a, b);
+    for (; r0 + 16 <= p; r0 += 16) fold_batch2<16, GDT, FULL, CONT>(gr, r0, e0, e1, L, a, b);
     if (r0 + 8 <= p) {
-      fold_batch2<8, GDT, CONT>(gr, r0, e0, e1, lane16, a, b);
+      fold_batch2<8, GDT, FULL, CONT>(gr, r0, e0, e1, L, a, b);
       r0 += 8;
     }
+  } else if constexpr (MAXB == 8) {
+    for (; r0 + 8 <= p; r0 += 8) fold_batch2<8, GDT, FULL, CONT>(gr, r0, e0, e1, L, a, b);
   } else {
-    static_assert(MAXB == 8, "rank batches of 16 or 8");
-    for (; r0 + 8 <= p; r0 += 8) fold_batch2<8, GDT, CONT>(gr, r0, e0, e1, lane16, a, b);
+    for (; r0 + 4 <= p; r0 += 4) fold_batch2<4, GDT, FULL, CONT>(gr, r0, e0, e1, L, a, b);
   }
   if (r0 + 4 <= p) {
-    fold_batch2<4, GDT, CONT>(gr, r0, e0, e1, lane16, a, b);
+    fold_batch2<4, GDT, FULL, CONT>(gr, r0, e0, e1, L, a, b);
     r0 += 4;
   }
   if (r0 + 2 <= p) {
-    fold_batch2<2, GDT, CONT>(gr, r0, e0, e1, lane16, a, b);
+    fold_batch2<2, GDT, FULL, CONT>(gr, r0, e0, e1, L, a, b);
     r0 += 2;
   }
-  if (r0 < p) fold_batch2<1, GDT, CONT>(gr, r0, e0, e1, lane16, a, b);
+  if (r0 < p) fold_batch2<1, GDT, FULL, CONT>(gr, r0, e0, e1, L, a, b);
 }
 
 // Rank-order mean of one element, kRankBatch loads in flight per batch.
@@ -388,17 +491,61 @@ __device__ __forceinline__ float mean1(const Grads& gr, int p, int64_t e, float 
   return s / PF;
 }
 
-// Adam + downcast of one lane's 8 elements at uniform element e0.  x holds
-// the fp32 gradient mean, or (DIVIDE) the rank sums, divided by P here.  The
-// sums are read, never written back: writing the quotients into the sum
-// registers before the update measurably worsens register allocation.
-template <int PDT, int FORM, bool PARAM = true, bool DIVIDE = false>
-__device__ __forceinline__ void adam8(const Consts& c, const float (&x)[kVec], float* w, float* m,
-                                      float* v, uint16_t* par, int64_t e0, uint32_t lane16,
-                                      uint32_t lane32) {
+// ---- the update of a group -------------------------------------------------
+// The state of one full group at e0: its loads are issued first
+// (load_group), then Adam and the downcast (apply_group) use them.  x: the
+// rank sums (divided by P here) or, DIVIDE false, the mean.
+struct GroupState {
+  f32x4 w0, w1, m0, m1, v0, v1;
+};
+
+template <int FORM>
+__device__ __forceinline__ GroupState load_group(const Lanes& L, const float* w, const float* m,
+                                                 const float* v, int64_t e0) {
+  return GroupState{ld_f32x4(w + e0, L.q32), ld_f32x4(w + e0, L.q32 + 1024u),
+                    ld_state<kUsesM<FORM>>(m + e0, L.q32),
+                    ld_state<kUsesM<FORM>>(m + e0, L.q32 + 1024u),
+                    ld_state<kUsesV<FORM>>(v + e0, L.q32),
+                    ld_state<kUsesV<FORM>>(v + e0, L.q32 + 1024u)};
+}
+
+template <int PDT, int FORM, bool DIVIDE = true, bool PARAM = true>
+__device__ __forceinline__ void apply_group(const Consts& c, const Lanes& L, const GroupState& q,
+                                            const float (&x)[kVec], float* w, float* m,
+                                            float* v, uint16_t* par, int64_t e0) {
+  float W[kVec] = {q.w0.x, q.w0.y, q.w0.z, q.w0.w, q.w1.x, q.w1.y, q.w1.z, q.w1.w};
+  float M[kVec] = {q.m0.x, q.m0.y, q.m0.z, q.m0.w, q.m1.x, q.m1.y, q.m1.z, q.m1.w};
+  float V[kVec] = {q.v0.x, q.v0.y, q.v0.z, q.v0.w, q.v1.x, q.v1.y, q.v1.z, q.v1.w};
+#pragma unroll
+  for (int j = 0; j < kVec; ++j) {
+    if constexpr (DIVIDE) {
+      adam1<FORM>(c, x[j] / c.PF, W[j], M[j], V[j]);
+    } else {
+      adam1<FORM>(c, x[j], W[j], M[j], V[j]);
+    }
+  }
   float* wb = w + e0;
   float* mb = m + e0;
   float* vb = v + e0;
+  st_f32x4(wb, L.q32, f32x4{W[0], W[1], W[2], W[3]});
+  st_f32x4(wb, L.q32 + 1024u, f32x4{W[4], W[5], W[6], W[7]});
+  st_state<kUsesM<FORM>>(mb, L.q32, f32x4{M[0], M[1], M[2], M[3]});
+  st_state<kUsesM<FORM>>(mb, L.q32 + 1024u, f32x4{M[4], M[5], M[6], M[7]});
+  st_state<kUsesV<FORM>>(vb, L.q32, f32x4{V[0], V[1], V[2], V[3]});
+  st_state<kUsesV<FORM>>(vb, L.q32 + 1024u, f32x4{V[4], V[5], V[6], V[7]});
+  if constexpr (PARAM) st_h8<PDT>(par + e0, L, W);
+}
+
+// The partial group: Adam + downcast of a lane's 8 consecutive elements at
+// e0 + 8 * lane.  x holds the fp32 gradient mean, or (DIVIDE) the rank sums,
+// divided by P here.
+template <int PDT, int FORM, bool PARAM = true, bool DIVIDE = false>
+__device__ __forceinline__ void adam8(const Consts& c, const float (&x)[kVec], float* w, float* m,
+                                      float* v, uint16_t* par, int64_t e0, const Lanes& L) {
+  float* wb = w + e0;
+  float* mb = m + e0;
+  float* vb = v + e0;
+  const uint32_t lane32 = L.c32;
   const f32x4 w0 = ld_f32x4(wb, lane32), w1 = ld_f32x4(wb, lane32 + 16);
   const f32x4 m0 = ld_state<kUsesM<FORM>>(mb, lane32), m1 = ld_state<kUsesM<FORM>>(mb, lane32 + 16);
   const f32x4 v0 = ld_state<kUsesV<FORM>>(vb, lane32), v1 = ld_state<kUsesV<FORM>>(vb, lane32 + 16);
@@ -420,96 +567,137 @@ __device__ __forceinline__ void adam8(const Consts& c, const float (&x)[kVec], f
   st_state<kUsesV<FORM>>(vb, lane32, f32x4{V[0], V[1], V[2], V[3]});
   st_state<kUsesV<FORM>>(vb, lane32 + 16, f32x4{V[4], V[5], V[6], V[7]});
   if constexpr (PARAM)
-    st_u16x8(par + e0, lane16,
+    st_u16x8(par + e0, L.c16,
              u32x4{narrow2<PDT>(W[0], W[1]), narrow2<PDT>(W[2], W[3]), narrow2<PDT>(W[4], W[5]),
                    narrow2<PDT>(W[6], W[7])});
 }
 
-// adam8 for two vectors per lane: the state loads of both are issued
-// together, then the arithmetic and stores of each.
-template <int PDT, int FORM, bool DIVIDE = true, bool PARAM = true>
+// Two groups (either map): both groups' state loads issued together, then
+// the arithmetic and stores of each.
+template <int PDT, int FORM, bool DIVIDE = true, bool PARAM = true, bool FULL = true>
 __device__ __forceinline__ void adam8x2(const Consts& c, const float (&a)[kVec],
                                         const float (&b)[kVec], float* w, float* m, float* v,
-                                        uint16_t* par, int64_t e0, int64_t e1, uint32_t lane16,
-                                        uint32_t lane32) {
-  f32x4 S[2][6];
+                                        uint16_t* par, int64_t e0, int64_t e1, const Lanes& L) {
+  if constexpr (FULL) {
+    const GroupState qa = load_group<FORM>(L, w, m, v, e0);
+    const GroupState qb = load_group<FORM>(L, w, m, v, e1);
+    __builtin_amdgcn_sched_barrier(0);
+    apply_group<PDT, FORM, DIVIDE, PARAM>(c, L, qa, a, w, m, v, par, e0);
+    apply_group<PDT, FORM, DIVIDE, PARAM>(c, L, qb, b, w, m, v, par, e1);
+  } else {
+    const uint32_t lane16 = L.c16, lane32 = L.c32;
+    f32x4 S[2][6];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int64_t e = q == 0 ? e0 : e1;
-    S[q][0] = ld_f32x4(w + e, lane32);
-    S[q][1] = ld_f32x4(w + e, lane32 + 16);
-    S[q][2] = ld_state<kUsesM<FORM>>(m + e, lane32);
-    S[q][3] = ld_state<kUsesM<FORM>>(m + e, lane32 + 16);
-    S[q][4] = ld_state<kUsesV<FORM>>(v + e, lane32);
-    S[q][5] = ld_state<kUsesV<FORM>>(v + e, lane32 + 16);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int64_t e = q == 0 ? e0 : e1;
-    const float(&x)[kVec] = q == 0 ? a : b;
-    float W[kVec] = {S[q][0].x, S[q][0].y, S[q][0].z, S[q][0].w,
-                     S[q][1].x, S[q][1].y, S[q][1].z, S[q][1].w};
-    float M[kVec] = {S[q][2].x, S[q][2].y, S[q][2].z, S[q][2].w,
-                     S[q][3].x, S[q][3].y, S[q][3].z, S[q][3].w};
-    float V[kVec] = {S[q][4].x, S[q][4].y, S[q][4].z, S[q][4].w,
-                     S[q][5].x, S[q][5].y, S[q][5].z, S[q][5].w};
-#pragma unroll
-    for (int j = 0; j < kVec; ++j) {
-      if constexpr (DIVIDE) {
-        adam1<FORM>(c, x[j] / c.PF, W[j], M[j], V[j]);
-      } else {
-        adam1<FORM>(c, x[j], W[j], M[j], V[j]);
-      }
+    for (int q = 0; q < 2; ++q) {
+      const int64_t e = q == 0 ? e0 : e1;
+      S[q][0] = ld_f32x4(w + e, lane32);
+      S[q][1] = ld_f32x4(w + e, lane32 + 16);
+      S[q][2] = ld_state<kUsesM<FORM>>(m + e, lane32);
+      S[q][3] = ld_state<kUsesM<FORM>>(m + e, lane32 + 16);
+      S[q][4] = ld_state<kUsesV<FORM>>(v + e, lane32);
+      S[q][5] = ld_state<kUsesV<FORM>>(v + e, lane32 + 16);
     }
-    st_f32x4(w + e, lane32, f32x4{W[0], W[1], W[2], W[3]});
-    st_f32x4(w + e, lane32 + 16, f32x4{W[4], W[5], W[6], W[7]});
-    st_state<kUsesM<FORM>>(m + e, lane32, f32x4{M[0], M[1], M[2], M[3]});
-    st_state<kUsesM<FORM>>(m + e, lane32 + 16, f32x4{M[4], M[5], M[6], M[7]});
-    st_state<kUsesV<FORM>>(v + e, lane32, f32x4{V[0], V[1], V[2], V[3]});
-    st_state<kUsesV<FORM>>(v + e, lane32 + 16, f32x4{V[4], V[5], V[6], V[7]});
-    if constexpr (PARAM)
-      st_u16x8(par + e, lane16,
-               u32x4{narrow2<PDT>(W[0], W[1]), narrow2<PDT>(W[2], W[3]), narrow2<PDT>(W[4], W[5]),
-                     narrow2<PDT>(W[6], W[7])});
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int64_t e = q == 0 ? e0 : e1;
+      const float(&x)[kVec] = q == 0 ? a : b;
+      float W[kVec] = {S[q][0].x, S[q][0].y, S[q][0].z, S[q][0].w,
+                       S[q][1].x, S[q][1].y, S[q][1].z, S[q][1].w};
+      float M[kVec] = {S[q][2].x, S[q][2].y, S[q][2].z, S[q][2].w,
+                       S[q][3].x, S[q][3].y, S[q][3].z, S[q][3].w};
+      float V[kVec] = {S[q][4].x, S[q][4].y, S[q][4].z, S[q][4].w,
+                       S[q][5].x, S[q][5].y, S[q][5].z, S[q][5].w};
+#pragma unroll
+      for (int j = 0; j < kVec; ++j) {
+        if constexpr (DIVIDE) {
+          adam1<FORM>(c, x[j] / c.PF, W[j], M[j], V[j]);
+        } else {
+          adam1<FORM>(c, x[j], W[j], M[j], V[j]);
+        }
+      }
+      st_f32x4(w + e, lane32, f32x4{W[0], W[1], W[2], W[3]});
+      st_f32x4(w + e, lane32 + 16, f32x4{W[4], W[5], W[6], W[7]});
+      st_state<kUsesM<FORM>>(m + e, lane32, f32x4{M[0], M[1], M[2], M[3]});
+      st_state<kUsesM<FORM>>(m + e, lane32 + 16, f32x4{M[4], M[5], M[6], M[7]});
+      st_state<kUsesV<FORM>>(v + e, lane32, f32x4{V[0], V[1], V[2], V[3]});
+      st_state<kUsesV<FORM>>(v + e, lane32 + 16, f32x4{V[4], V[5], V[6], V[7]});
+      if constexpr (PARAM)
+        st_u16x8(par + e, lane16,
+                 u32x4{narrow2<PDT>(W[0], W[1]), narrow2<PDT>(W[2], W[3]),
+                       narrow2<PDT>(W[4], W[5]), narrow2<PDT>(W[6], W[7])});
+    }
   }
 }
 
-// The part of a shard that whole kGroupsMax chunks do not cover: the leftover
-// groups (two vectors of 8 elements per lane, 2 * kBlock vectors per piece) and the
-// scalar head and tail elements.  left0 is the first vector after the whole
-// chunks.  Whole chunks go round-robin, so blocks nfull % nblk, ... have one
-// chunk fewer than the rest: the pieces are dealt out starting there, then the
-// scalar elements go to the next block.  Both read the ranks in batches
-// (several loads in flight per lane): a piece is too small to batch over
-// groups, and one load at a time would cost a full memory round trip per rank.
-template <int GDT, int PDT, int FORM, int MAXB = 16, class Grads>
+// ---- the rest of a range ---------------------------------------------------
+// What whole kGroupsMax chunks do not cover, from vector left0 on (vectors of
+// 8 elements after the head h): its full groups in pieces of two, then one
+// full group if their count is odd, then the partial group, dealt one item
+// per block.  Whole chunks go round-robin, so blocks nfull % nblk, ... have
+// one chunk fewer than the rest: the items are dealt out starting there, then
+// the scalar head and tail elements go to the next block.  All read the
+// ranks in batches (several loads in flight per lane): an item is too small
+// to batch over groups, and one load at a time would cost a full memory
+// round trip per rank.
+struct RestPlan {
+  int64_t first_full;  // vector of the first full group
+  int64_t nfg;         // full groups
+  int64_t part;        // vectors in the partial group (0..kBlock-1)
+  int64_t npairs;      // two-group pieces
+  int64_t nitems;      // pieces, the odd full group, the partial group
+  int64_t me;          // this block's place in the deal
+};
+
+__device__ __forceinline__ RestPlan rest_plan(int64_t nvec, int64_t left0, int64_t nfull,
+                                              int64_t blk, int64_t nblk) {
+  RestPlan r;
+  r.first_full = left0;
+  r.nfg = (nvec - left0) / kBlock;
+  r.part = (nvec - left0) % kBlock;
+  r.npairs = r.nfg / 2;
+  r.nitems = r.npairs + (r.nfg & 1) + (r.part > 0 ? 1 : 0);
+  const int64_t first = nfull % nblk;
+  r.me = (blk - first + nblk) % nblk;
+  return r;
+}
+
+// FULL picks the lane map of full groups (the contiguous one measured faster
+// in the four-workgroup small-shard kernel).
+template <int GDT, int PDT, int FORM, int MAXB = 16, bool FULL = true, class Grads>
 __device__ __forceinline__ void fused_rest(const Grads& gr, int p, float* __restrict__ w,
                                            float* __restrict__ m, float* __restrict__ v,
                                            uint16_t* __restrict__ par, int64_t len, int64_t h,
                                            int64_t nvec, int64_t left0, int64_t nfull,
                                            const Consts& c, int64_t blk, int64_t nblk,
-                                           uint32_t lane16, uint32_t lane32) {
+                                           const Lanes& L) {
   const int tid = threadIdx.x;
-  const int64_t first = nfull % nblk;
-  const int64_t me = (blk - first + nblk) % nblk;  // this block's rank in the deal
-  constexpr int64_t kPiece = 2 * kBlock;  // vectors per piece: two per lane
-  const int64_t npieces = (nvec - left0 + kPiece - 1) / kPiece;
-  for (int64_t i = me; i < npieces; i += nblk) {
-    const int64_t gb = left0 + i * kPiece;
-    const int64_t e0 = h + gb * kVec;
-    const int64_t e1 = e0 + static_cast<int64_t>(kBlock) * kVec;
-    if (gb + kBlock + tid < nvec) {
+  const RestPlan R = rest_plan(nvec, left0, nfull, blk, nblk);
+  for (int64_t i = R.me; i < R.nitems; i += nblk) {
+    if (i < R.npairs) {
+      const int64_t e0 = h + (R.first_full + 2 * i * kBlock) * kVec;
+      const int64_t e1 = e0 + kGroup;
       float a[kVec], b[kVec];
-      sum_ranks8x2<GDT, MAXB>(gr, p, e0, e1, lane16, a, b);
-      adam8x2<PDT, FORM>(c, a, b, w, m, v, par, e0, e1, lane16, lane32);
-    } else if (gb + tid < nvec) {
+      sum_ranks8x2<GDT, MAXB, FULL>(gr, p, e0, e1, L, a, b);
+      adam8x2<PDT, FORM, true, true, FULL>(c, a, b, w, m, v, par, e0, e1, L);
+    } else if (i == R.npairs && (R.nfg & 1)) {
+      const int64_t e0 = h + (R.first_full + 2 * R.npairs * kBlock) * kVec;
       float g[kVec];
-      sum_ranks8<GDT>(gr, p, e0, lane16, g);
-      adam8<PDT, FORM, true, true>(c, g, w, m, v, par, e0, lane16, lane32);
+      sum_ranks8<GDT, FULL, false, MAXB>(gr, p, e0, L, g);
+      if constexpr (FULL) {
+        const GroupState q = load_group<FORM>(L, w, m, v, e0);
+        apply_group<PDT, FORM>(c, L, q, g, w, m, v, par, e0);
+      } else {
+        adam8<PDT, FORM, true, true>(c, g, w, m, v, par, e0, L);
+      }
+    } else if (tid < R.part) {
+      const int64_t e0 = h + (R.first_full + R.nfg * kBlock) * kVec;
+      float g[kVec];
+      sum_ranks8<GDT, false, false, MAXB>(gr, p, e0, L, g);
+      adam8<PDT, FORM, true, true>(c, g, w, m, v, par, e0, L);
     }
   }
-  if (me == npieces % nblk) {
+  if (R.me == R.nitems % nblk) {
     const int64_t t0 = h + nvec * kVec;
     const int64_t nsc = h + (len - t0);
     for (int64_t i = tid; i < nsc; i += kBlock) {

@@ -10,12 +10,23 @@ namespace {
 
 // Single-tensor fused step, one workgroup per CU.  The loop over whole chunks
 // (nearly all of the bytes) is written out in the kernel body instead of going
-// through read_chunk / update_chunk: when the per-group sums cross a function
+// through helper functions: when the per-group sums cross a function
 // boundary by reference, the callee is optimised on its own before inlining
 // and the compiler peels the first rank out of the rank loop; the resulting
 // schedule measured about 11% slower on MI355X (3.17 ms against 2.85 ms on a
 // 117M-element, 64-rank shard) with bit-identical results.  Kept in this
 // shape, the rank loop tests r == 0 per group and keeps a single loop body.
+//
+// The whole chunks keep the contiguous lane map (8 consecutive elements per
+// lane, one 16-byte load per rank and group) rather than the full-group map
+// of the other kernels.  Measured on the 117M-element, 64-rank shard, the
+// full-group map makes each phase faster alone (reads 2.33 -> 2.29 ms,
+// update 0.67 -> 0.60 ms) but the step slower (2.78 -> 2.85-2.89 ms): its
+// dense full-line store bursts overlap worse with other CUs' read phases.
+// The price of this map is that each store instruction writes half of every
+// cache line it touches, and about 5% of the written bytes are repeated.
+// The loop is also sensitive to its exact shape: scheduling barriers that
+// force each load's issue order made it 9% slower (3.03 ms).
 template <int GDT, int PDT, int FORM, int PMAX>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fused_kernel(GradArgs<PMAX> ga, int p, float* __restrict__ w, float* __restrict__ m,
@@ -111,14 +122,15 @@ void fused_kernel(GradArgs<PMAX> ga, int p, float* __restrict__ w, float* __rest
     }
   }
   fused_rest<GDT, PDT, FORM>(gr, p, w, m, v, par, len, h, nvec, nfull * kFull, nfull, c,
-                             blockIdx.x, gridDim.x, lane16, lane32);
+                             blockIdx.x, gridDim.x, lanes());
 }
 
 // Single-tensor fused step for shards under half a whole chunk per CU, where
-// fused_kernel would run no whole chunk at all: the same two-vector pieces,
-// dealt over four workgroups per CU (four waves per SIMD, rank batches of at
-// most 8 so that no register spills).  On the 16-rank, 6.25M-element shards
-// this is 4% faster than one workgroup per CU.
+// fused_kernel would run no whole chunk at all: the same pieces of two
+// groups, dealt over four workgroups per CU (four waves per SIMD), in the
+// full-group lane map with rank batches of 4.  On the 16-rank,
+// 6.25M-element shards: 64.4 us against 66.6 (contiguous map, batches of 8)
+// and 68.8 (contiguous, 4); four workgroups per CU were 4% faster than one.
 template <int GDT, int PDT, int FORM, int PMAX>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kSmallWaves)))
 void small_kernel(GradArgs<PMAX> ga, int p, float* __restrict__ w, float* __restrict__ m,
@@ -128,8 +140,8 @@ void small_kernel(GradArgs<PMAX> ga, int p, float* __restrict__ w, float* __rest
   const ArgGrads gr = rank_grads(rank_table);
   const int64_t h = head < len ? head : len;
   const int64_t nvec = (len - h) / kVec;
-  fused_rest<GDT, PDT, FORM, 8>(gr, p, w, m, v, par, len, h, nvec, 0, 0, c, blockIdx.x,
-                                gridDim.x, threadIdx.x * 16u, threadIdx.x * 32u);
+  fused_rest<GDT, PDT, FORM, 4, true>(gr, p, w, m, v, par, len, h, nvec, 0, 0, c, blockIdx.x,
+                                       gridDim.x, lanes());
 }
 
 }  // namespace

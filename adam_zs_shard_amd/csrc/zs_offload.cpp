@@ -20,8 +20,9 @@
 //   compute stream:  mean of the P ranks over [lo, hi), rounded -> g16_dev
 //   d2h stream:      waits for that mean, copies it to g16_host[slot]
 //   host:            waits for the copy (PLAIN) or not (DELAYED: the
-//                    gradient is the one received last step), runs the
-//                    update on `threads` threads into param_host
+//                    gradient is the one received last step); `threads`
+//                    workers, started once per call, update the bucket
+//                    into param_host
 //   h2d stream:      copies param_host[lo, hi) into the working copy
 // The call returns when every copy and update it started is complete.
 
@@ -29,6 +30,9 @@
 
 #include <algorithm>
 #include <cmath>
+#include <condition_variable>
+#include <mutex>
+#include <thread>
 #include <vector>
 
 #include "../../include/zshard.h"
@@ -172,28 +176,89 @@ extern "C" zs_status zs_offload_step(const zs_offload_args* a, const zs_adam_hpa
     if (err != hipSuccess) return fail(err);
   }
   // 2. the host update, bucket by bucket, each bucket's parameters sent back
-  // as soon as they are ready
+  // as soon as they are ready.  One set of worker threads for the whole call
+  // (starting threads per bucket cost more than small buckets take): worker t
+  // updates its share of every bucket in turn, as soon as the bucket's
+  // gradient is in host memory; this thread waits for the copies, releases
+  // the buckets, and queues each bucket's parameter copy when every worker
+  // has finished it.
   if (update) {
     const auto* g16h_use = static_cast<const uint16_t*>(
         mode == ZS_OFFLOAD_DELAYED ? a->g16_host[1 - slot] : a->g16_host[slot]);
     auto* ph = static_cast<uint16_t*>(a->param_host);
-    for (int64_t b = 0; b < nb; ++b) {
+    int64_t nt = a->threads > 0 ? a->threads
+                                : static_cast<int64_t>(std::thread::hardware_concurrency());
+    nt = std::max<int64_t>(1, std::min<int64_t>(nt, (bucket + 65535) / 65536));
+    std::mutex mu;
+    std::condition_variable cv_ready, cv_done;
+    int64_t ready = mode == ZS_OFFLOAD_DELAYED ? nb : 0;  // buckets whose gradient is here
+    std::vector<int64_t> done(static_cast<size_t>(nb), 0);  // workers finished per bucket
+    zs_status worker_status = ZS_OK;
+    auto work = [&](int64_t t) {
+      for (int64_t b = 0; b < nb; ++b) {
+        {
+          std::unique_lock<std::mutex> lk(mu);
+          cv_ready.wait(lk, [&] { return ready > b || worker_status != ZS_OK; });
+          if (worker_status != ZS_OK) return;
+        }
+        const int64_t lo = b * bucket, hi = std::min(len, lo + bucket);
+        // contiguous shares on 16-element (64-byte fp32 line) boundaries
+        const int64_t per = ((hi - lo + nt - 1) / nt + 15) / 16 * 16;
+        const int64_t a0 = std::min(hi, lo + t * per), a1 = std::min(hi, a0 + per);
+        zs_status st = ZS_OK;
+        if (a0 < a1)
+          st = zs_cpu_adam_step(g16h_use + a0, a->grad_dtype, a->w + a0,
+                                um ? a->m + a0 : nullptr, uv ? a->v + a0 : nullptr, ph + a0,
+                                a->param_dtype, a1 - a0, hp, 1);
+        std::lock_guard<std::mutex> lk(mu);
+        if (st != ZS_OK && worker_status == ZS_OK) worker_status = st;
+        ++done[static_cast<size_t>(b)];
+        cv_done.notify_all();
+        if (worker_status != ZS_OK) {
+          cv_ready.notify_all();
+          return;
+        }
+      }
+    };
+    std::vector<std::thread> pool;
+    for (int64_t t = 0; t < nt; ++t) pool.emplace_back(work, t);
+    zs_status st = ZS_OK;
+    for (int64_t b = 0; b < nb && st == ZS_OK; ++b) {
       const int64_t lo = b * bucket, hi = std::min(len, lo + bucket);
       if (mode == ZS_OFFLOAD_PLAIN) {
         err = hipEventSynchronize(copied.ev[b]);
-        if (err != hipSuccess) return fail(err);
+        std::lock_guard<std::mutex> lk(mu);
+        if (err != hipSuccess) {
+          st = fail(err);
+          worker_status = st;
+        } else {
+          ready = b + 1;
+        }
+        cv_ready.notify_all();
+        if (st != ZS_OK) break;
       }
-      const zs_status st = zs_cpu_adam_step(g16h_use + lo, a->grad_dtype, a->w + lo,
-                                            um ? a->m + lo : nullptr, uv ? a->v + lo : nullptr,
-                                            ph + lo, a->param_dtype, hi - lo, hp, a->threads);
-      if (st != ZS_OK) {
-        (void)hipStreamSynchronize(ds);
-        (void)hipStreamSynchronize(hs);
-        return st;
+      {
+        std::unique_lock<std::mutex> lk(mu);
+        cv_done.wait(lk, [&] { return done[static_cast<size_t>(b)] == nt || worker_status != ZS_OK; });
+        if (worker_status != ZS_OK) {
+          st = worker_status;
+          break;
+        }
       }
       err = hipMemcpyAsync(par_dev + lo, ph + lo, 2u * static_cast<size_t>(hi - lo),
                            hipMemcpyHostToDevice, hs);
-      if (err != hipSuccess) return fail(err);
+      if (err != hipSuccess) {
+        st = fail(err);
+        std::lock_guard<std::mutex> lk(mu);
+        worker_status = st;
+        cv_ready.notify_all();
+      }
+    }
+    for (auto& th : pool) th.join();
+    if (st != ZS_OK) {
+      (void)hipStreamSynchronize(ds);
+      (void)hipStreamSynchronize(hs);
+      return st;
     }
   }
   // 3. everything this call started is complete before it returns

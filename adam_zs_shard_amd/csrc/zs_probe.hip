@@ -178,6 +178,12 @@ int32_t zsp_stream(int32_t mix, const void* src, void* dst, int64_t stream_bytes
     case ZSP_PHASED_2_1: if (!dst) return 1; e = run_phased<2, 1, 16>(src, dst, stream_bytes, nvec, grid, sink, s); break;
     case ZSP_PHASED_22_7: if (!dst) return 1; e = run_phased<22, 7, 16>(src, dst, stream_bytes, nvec, grid, sink, s); break;
     case ZSP_PHASED_10_1: if (!dst) return 1; e = run_phased<10, 1, 16>(src, dst, stream_bytes, nvec, grid, sink, s); break;
+    // pure reads: streams x loads in flight per stream
+    case ZSP_READ1_U16: e = run<1, 0, 16>(src, dst, stream_bytes, nvec, grid, sink, s); break;
+    case ZSP_READ2_U8: e = run<2, 0, 8>(src, dst, stream_bytes, nvec, grid, sink, s); break;
+    case ZSP_READ4_U8: e = run<4, 0, 8>(src, dst, stream_bytes, nvec, grid, sink, s); break;
+    case ZSP_READ8_U8: e = run<8, 0, 8>(src, dst, stream_bytes, nvec, grid, sink, s); break;
+    case ZSP_READ1_U32: e = run<1, 0, 32>(src, dst, stream_bytes, nvec, grid, sink, s); break;
     default: return 1;
   }
   return e == hipSuccess ? 0 : 2;
@@ -185,8 +191,9 @@ int32_t zsp_stream(int32_t mix, const void* src, void* dst, int64_t stream_bytes
 
 int32_t zsp_streams(int32_t mix, int32_t* nread, int32_t* nwrite) {
   static const int32_t tab[][2] = {{8, 0}, {1, 1}, {2, 1}, {22, 7}, {10, 1},
-                                   {8, 0}, {1, 1}, {2, 1}, {22, 7}, {10, 1}};
-  if (mix < 0 || mix > ZSP_PHASED_10_1 || !nread || !nwrite) return 1;
+                                   {8, 0}, {1, 1}, {2, 1}, {22, 7}, {10, 1},
+                                   {1, 0}, {2, 0}, {4, 0}, {8, 0}, {1, 0}};
+  if (mix < 0 || mix > ZSP_READ1_U32 || !nread || !nwrite) return 1;
   *nread = tab[mix][0];
   *nwrite = tab[mix][1];
   return 0;

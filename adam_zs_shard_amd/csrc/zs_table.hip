@@ -24,8 +24,7 @@ void table_kernel(TableSrc src, int p, Consts c0, const StepTableDev* st) {
     }
     c = step_consts(st)[at];
   }
-  const uint32_t lane16 = threadIdx.x * 16u;
-  const uint32_t lane32 = threadIdx.x * 32u;
+  const Lanes L = lanes();
   constexpr int64_t kFull = static_cast<int64_t>(kBlock) * kGroupsMax;
   for (int64_t item = src.first(); item < src.count(); item += src.stride()) {
     const auto R = src.open(item);
@@ -49,7 +48,7 @@ void table_kernel(TableSrc src, int p, Consts c0, const StepTableDev* st) {
         // queued behind the miss fills the per-CU translation queue and stalls
         // every wave's loads).
         {
-          const u32x4 q0 = ld_grad(base, lane16);
+          const G8 q0 = ld_g8(base, L);
           __builtin_amdgcn_sched_barrier(0);
           if (r == 0) {
             init8<GDT>(s[0], q0);
@@ -59,10 +58,12 @@ void table_kernel(TableSrc src, int p, Consts c0, const StepTableDev* st) {
           __builtin_amdgcn_sched_barrier(0);
         }
         {  // groups 1 .. kTableLoadBatch-1
-          u32x4 q[kTableLoadBatch - 1];
+          G8 q[kTableLoadBatch - 1];
 #pragma unroll
-          for (int u = 0; u < kTableLoadBatch - 1; ++u)
-            q[u] = ld_grad(base + static_cast<int64_t>(1 + u) * kBlock * kVec, lane16);
+          for (int u = 0; u < kTableLoadBatch - 1; ++u) {
+            q[u] = ld_g8(base + (1 + u) * kGroup, L);
+            __builtin_amdgcn_sched_barrier(0);  // issued in group order
+          }
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int u = 0; u < kTableLoadBatch - 1; ++u) {
@@ -71,15 +72,18 @@ void table_kernel(TableSrc src, int p, Consts c0, const StepTableDev* st) {
             } else {
               fold8<GDT>(s[1 + u], q[u]);
             }
+            __builtin_amdgcn_sched_barrier(0);  // fold in load order
           }
           __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int u0 = kTableLoadBatch; u0 < kGroupsMax; u0 += kTableLoadBatch) {
-          u32x4 q[kTableLoadBatch];
+          G8 q[kTableLoadBatch];
 #pragma unroll
-          for (int u = 0; u < kTableLoadBatch; ++u)
-            q[u] = ld_grad(base + static_cast<int64_t>(u0 + u) * kBlock * kVec, lane16);
+          for (int u = 0; u < kTableLoadBatch; ++u) {
+            q[u] = ld_g8(base + (u0 + u) * kGroup, L);
+            __builtin_amdgcn_sched_barrier(0);  // issued in group order
+          }
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int u = 0; u < kTableLoadBatch; ++u) {
@@ -88,58 +92,23 @@ void table_kernel(TableSrc src, int p, Consts c0, const StepTableDev* st) {
             } else {
               fold8<GDT>(s[u0 + u], q[u]);
             }
+            __builtin_amdgcn_sched_barrier(0);  // fold in load order
           }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      // update phase: mean, Adam, stores, kUG groups at a time.  One group,
-      // as in fused_kernel: with two groups' state loads in flight the 8-rank
-      // Llama-3-8B shard ran 0.7% slower and wrote 11% more bytes to HBM than
-      // the model (one group: 4.5%).
-      constexpr int kUG = 1;
-      static_assert(kGroupsMax % kUG == 0, "whole update batches per chunk");
+      // update phase: mean, Adam, stores, group by group
 #pragma unroll
-      for (int u0 = 0; u0 < kGroupsMax; u0 += kUG) {
-        f32x4 A[kUG][6];
-#pragma unroll
-        for (int q = 0; q < kUG; ++q) {
-          const int64_t e0 = h + (g0 + static_cast<int64_t>(u0 + q) * kBlock) * kVec;
-          A[q][0] = ld_f32x4(w + e0, lane32);
-          A[q][1] = ld_f32x4(w + e0, lane32 + 16);
-          A[q][2] = ld_state<kUsesM<FORM>>(m + e0, lane32);
-          A[q][3] = ld_state<kUsesM<FORM>>(m + e0, lane32 + 16);
-          A[q][4] = ld_state<kUsesV<FORM>>(v + e0, lane32);
-          A[q][5] = ld_state<kUsesV<FORM>>(v + e0, lane32 + 16);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int q = 0; q < kUG; ++q) {
-          const int u = u0 + q;
-          const int64_t e0 = h + (g0 + static_cast<int64_t>(u) * kBlock) * kVec;
-          float W[kVec] = {A[q][0].x, A[q][0].y, A[q][0].z, A[q][0].w, A[q][1].x, A[q][1].y, A[q][1].z, A[q][1].w};
-          float M[kVec] = {A[q][2].x, A[q][2].y, A[q][2].z, A[q][2].w, A[q][3].x, A[q][3].y, A[q][3].z, A[q][3].w};
-          float V[kVec] = {A[q][4].x, A[q][4].y, A[q][4].z, A[q][4].w, A[q][5].x, A[q][5].y, A[q][5].z, A[q][5].w};
-#pragma unroll
-          for (int j = 0; j < kVec; ++j) adam1<FORM>(c, s[u][j] / c.PF, W[j], M[j], V[j]);
-          st_f32x4(w + e0, lane32, f32x4{W[0], W[1], W[2], W[3]});
-          st_f32x4(w + e0, lane32 + 16, f32x4{W[4], W[5], W[6], W[7]});
-          st_state<kUsesM<FORM>>(m + e0, lane32, f32x4{M[0], M[1], M[2], M[3]});
-          st_state<kUsesM<FORM>>(m + e0, lane32 + 16, f32x4{M[4], M[5], M[6], M[7]});
-          st_state<kUsesV<FORM>>(v + e0, lane32, f32x4{V[0], V[1], V[2], V[3]});
-          st_state<kUsesV<FORM>>(v + e0, lane32 + 16, f32x4{V[4], V[5], V[6], V[7]});
-          st_u16x8(par + e0, lane16,
-                   u32x4{narrow2<PDT>(W[0], W[1]), narrow2<PDT>(W[2], W[3]),
-                         narrow2<PDT>(W[4], W[5]), narrow2<PDT>(W[6], W[7])});
-        }
-        __builtin_amdgcn_sched_barrier(0);
+      for (int u = 0; u < kGroupsMax; ++u) {
+        const int64_t e0 = h + (g0 + static_cast<int64_t>(u) * kBlock) * kVec;
+        const GroupState q = load_group<FORM>(L, w, m, v, e0);
+        apply_group<PDT, FORM>(c, L, q, s[u], w, m, v, par, e0);
       }
     }
-    // fp16 gradients take rank batches of 8 in the pieces: with 16 the
-    // fp16 Adam instances spill 272 bytes; 8 leaves 44 and makes short-chunk
-    // fp16 tables 5% faster (GPT-2 shard 7); bf16 keeps 16.
-    fused_rest<GDT, PDT, FORM, GDT == kF16 ? 8 : 16>(gr, p, w, m, v, par, R.len, h, nvec,
-                                                     nfull * kFull, nfull, c, R.blk, R.nblk,
-                                                     lane16, lane32);
+    // the rest in rank batches of 8 (1% faster than 16 on the 35-piece GPT-2
+    // shard; with fp16 gradients, 16 spilled)
+    fused_rest<GDT, PDT, FORM, 8>(gr, p, w, m, v, par, R.len, h, nvec,
+                                                     nfull * kFull, nfull, c, R.blk, R.nblk, L);
   }
 }
 

@@ -34,25 +34,31 @@ struct MeanOut {
   void* out;
   int last;
   float PF;
-  // the 8 consecutive elements at e0 of one lane (lane16 = 16 * lane)
-  __device__ __forceinline__ void put8(int64_t e0, uint32_t lane16, const float (&s)[kVec]) const {
-    if (last) {
-      float g[kVec];
+  // one lane's 8 elements of the group at e0, in the full-group map (FULL)
+  // or 8 consecutive elements (the partial group)
+  template <bool FULL>
+  __device__ __forceinline__ void put8(int64_t e0, const Lanes& L, const float (&s)[kVec]) const {
+    float g[kVec];
 #pragma unroll
-      for (int j = 0; j < kVec; ++j) g[j] = s[j] / PF;
-      if constexpr (ODT == 0) {
-        float* o = static_cast<float*>(out) + e0;
-        st_f32x4(o, 2 * lane16, f32x4{g[0], g[1], g[2], g[3]});
-        st_f32x4(o, 2 * lane16 + 16, f32x4{g[4], g[5], g[6], g[7]});
+    for (int j = 0; j < kVec; ++j) g[j] = last ? s[j] / PF : s[j];
+    if (last && ODT != 0) {
+      constexpr int DT = ODT == 0 ? kF16 : ODT;
+      uint16_t* o = static_cast<uint16_t*>(out) + e0;
+      if constexpr (FULL) {
+        st_h8<DT>(o, L, g);
       } else {
-        st_u16x8(static_cast<uint16_t*>(out) + e0, lane16,
-                 u32x4{narrow2<ODT>(g[0], g[1]), narrow2<ODT>(g[2], g[3]),
-                       narrow2<ODT>(g[4], g[5]), narrow2<ODT>(g[6], g[7])});
+        st_u16x8(o, L.c16,
+                 u32x4{narrow2<DT>(g[0], g[1]), narrow2<DT>(g[2], g[3]),
+                       narrow2<DT>(g[4], g[5]), narrow2<DT>(g[6], g[7])});
       }
     } else {
       float* o = static_cast<float*>(out) + e0;
-      st_f32x4(o, 2 * lane16, f32x4{s[0], s[1], s[2], s[3]});
-      st_f32x4(o, 2 * lane16 + 16, f32x4{s[4], s[5], s[6], s[7]});
+      if constexpr (FULL) {
+        st_f8(o, L, g);
+      } else {
+        st_f32x4(o, L.c32, f32x4{g[0], g[1], g[2], g[3]});
+        st_f32x4(o, L.c32 + 16, f32x4{g[4], g[5], g[6], g[7]});
+      }
     }
   }
   __device__ __forceinline__ void put1(int64_t e, float s) const {
@@ -66,12 +72,18 @@ struct MeanOut {
   }
 };
 
-// The fp32 sums of earlier passes for one lane's 8 elements at e0.
-__device__ __forceinline__ void load_acc8(const float* acc, int64_t e0, uint32_t lane32,
+// The fp32 sums of earlier passes for one lane's 8 elements of the group at
+// e0, in either map.
+template <bool FULL>
+__device__ __forceinline__ void load_acc8(const float* acc, int64_t e0, const Lanes& L,
                                           float (&s)[kVec]) {
-  const f32x4 a = ld_f32x4(acc + e0, lane32), b = ld_f32x4(acc + e0, lane32 + 16);
-  s[0] = a.x; s[1] = a.y; s[2] = a.z; s[3] = a.w;
-  s[4] = b.x; s[5] = b.y; s[6] = b.z; s[7] = b.w;
+  if constexpr (FULL) {
+    ld_f8(acc + e0, L, s);
+  } else {
+    const f32x4 a = ld_f32x4(acc + e0, L.c32), b = ld_f32x4(acc + e0, L.c32 + 16);
+    s[0] = a.x; s[1] = a.y; s[2] = a.z; s[3] = a.w;
+    s[4] = b.x; s[5] = b.y; s[6] = b.z; s[7] = b.w;
+  }
 }
 
 // Rank-order sum of one element over this pass's p ranks, continuing the
@@ -98,46 +110,55 @@ __device__ __forceinline__ float sum1(const Grads& gr, int p, int64_t e, bool co
   return s;
 }
 
-// The stored mean's counterpart of fused_rest: the pieces left after the
-// whole chunks, then the scalar head and tail, dealt the same way.
+// One group's sums (either map), continuing acc when set.
+template <int GDT, bool FULL, class Grads>
+__device__ __forceinline__ void group_sums(const Grads& gr, int p, const float* acc, int64_t e0,
+                                           const Lanes& L, float (&g)[kVec]) {
+  if (acc) {
+    load_acc8<FULL>(acc, e0, L, g);
+    sum_ranks8<GDT, FULL, true>(gr, p, e0, L, g);
+  } else {
+    sum_ranks8<GDT, FULL>(gr, p, e0, L, g);
+  }
+}
+
+// The stored mean's counterpart of fused_rest: the groups left after the
+// whole chunks (pairs, the odd full group, the partial group), then the
+// scalar head and tail, dealt the same way.
 template <int GDT, int ODT, class Grads>
 __device__ __forceinline__ void mean_rest(const Grads& gr, int p, const float* acc,
                                           const MeanOut<ODT>& mo, int64_t len, int64_t h,
                                           int64_t nvec, int64_t left0, int64_t nfull,
-                                          int64_t blk, int64_t nblk, uint32_t lane16,
-                                          uint32_t lane32) {
+                                          int64_t blk, int64_t nblk, const Lanes& L) {
   const int tid = threadIdx.x;
-  const int64_t first = nfull % nblk;
-  const int64_t me = (blk - first + nblk) % nblk;
-  constexpr int64_t kPiece = 2 * kBlock;
-  const int64_t npieces = (nvec - left0 + kPiece - 1) / kPiece;
-  for (int64_t i = me; i < npieces; i += nblk) {
-    const int64_t gb = left0 + i * kPiece;
-    const int64_t e0 = h + gb * kVec;
-    const int64_t e1 = e0 + static_cast<int64_t>(kBlock) * kVec;
-    if (gb + kBlock + tid < nvec) {
+  const RestPlan R = rest_plan(nvec, left0, nfull, blk, nblk);
+  for (int64_t i = R.me; i < R.nitems; i += nblk) {
+    if (i < R.npairs) {
+      const int64_t e0 = h + (R.first_full + 2 * i * kBlock) * kVec;
+      const int64_t e1 = e0 + kGroup;
       float a[kVec], b[kVec];
       if (acc) {
-        load_acc8(acc, e0, lane32, a);
-        load_acc8(acc, e1, lane32, b);
-        sum_ranks8x2<GDT, 16, true>(gr, p, e0, e1, lane16, a, b);
+        load_acc8<true>(acc, e0, L, a);
+        load_acc8<true>(acc, e1, L, b);
+        sum_ranks8x2<GDT, 16, true, true>(gr, p, e0, e1, L, a, b);
       } else {
-        sum_ranks8x2<GDT>(gr, p, e0, e1, lane16, a, b);
+        sum_ranks8x2<GDT>(gr, p, e0, e1, L, a, b);
       }
-      mo.put8(e0, lane16, a);
-      mo.put8(e1, lane16, b);
-    } else if (gb + tid < nvec) {
+      mo.template put8<true>(e0, L, a);
+      mo.template put8<true>(e1, L, b);
+    } else if (i == R.npairs && (R.nfg & 1)) {
+      const int64_t e0 = h + (R.first_full + 2 * R.npairs * kBlock) * kVec;
       float g[kVec];
-      if (acc) {
-        load_acc8(acc, e0, lane32, g);
-        sum_ranks8<GDT, true>(gr, p, e0, lane16, g);
-      } else {
-        sum_ranks8<GDT>(gr, p, e0, lane16, g);
-      }
-      mo.put8(e0, lane16, g);
+      group_sums<GDT, true>(gr, p, acc, e0, L, g);
+      mo.template put8<true>(e0, L, g);
+    } else if (tid < R.part) {
+      const int64_t e0 = h + (R.first_full + R.nfg * kBlock) * kVec;
+      float g[kVec];
+      group_sums<GDT, false>(gr, p, acc, e0, L, g);
+      mo.template put8<false>(e0, L, g);
     }
   }
-  if (me == npieces % nblk) {
+  if (R.me == R.nitems % nblk) {
     const int64_t t0 = h + nvec * kVec;
     const int64_t nsc = h + (len - t0);
     for (int64_t i = tid; i < nsc; i += kBlock) {
@@ -161,8 +182,7 @@ void mean_chunk_kernel(GradArgs<PMAX> ga, int p, const float* acc, MeanOut<ODT> 
   const ArgGrads gr = kernarg_grads();
   const int64_t h = head < len ? head : len;
   const int64_t nvec = (len - h) / kVec;
-  const uint32_t lane16 = threadIdx.x * 16u;
-  const uint32_t lane32 = threadIdx.x * 32u;
+  const Lanes L = lanes();
   constexpr int64_t kFull = static_cast<int64_t>(kBlock) * kGroupsMax;
   const int64_t nfull = whole_chunks(nvec / kFull, gridDim.x);
   const bool cont = acc != nullptr;
@@ -172,13 +192,13 @@ void mean_chunk_kernel(GradArgs<PMAX> ga, int p, const float* acc, MeanOut<ODT> 
     if (cont) {
 #pragma unroll
       for (int u = 0; u < kGroupsMax; ++u)
-        load_acc8(acc, h + (g0 + static_cast<int64_t>(u) * kBlock) * kVec, lane32, s[u]);
+        load_acc8<true>(acc, h + (g0 + static_cast<int64_t>(u) * kBlock) * kVec, L, s[u]);
     }
     for (int r = 0; r < p; ++r) {
       const uint16_t* base = gr.get(r) + h + g0 * kVec;
       const bool start = !cont && r == 0;
       {
-        const u32x4 q0 = ld_grad(base, lane16);
+        const G8 q0 = ld_g8(base, L);
         __builtin_amdgcn_sched_barrier(0);
         if (start) {
           init8<GDT>(s[0], q0);
@@ -188,10 +208,12 @@ void mean_chunk_kernel(GradArgs<PMAX> ga, int p, const float* acc, MeanOut<ODT> 
         __builtin_amdgcn_sched_barrier(0);
       }
       {
-        u32x4 q[kLoadBatch - 1];
+        G8 q[kLoadBatch - 1];
 #pragma unroll
-        for (int u = 0; u < kLoadBatch - 1; ++u)
-          q[u] = ld_grad(base + static_cast<int64_t>(1 + u) * kBlock * kVec, lane16);
+        for (int u = 0; u < kLoadBatch - 1; ++u) {
+          q[u] = ld_g8(base + (1 + u) * kGroup, L);
+          __builtin_amdgcn_sched_barrier(0);  // issued in group order
+        }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < kLoadBatch - 1; ++u) {
@@ -200,43 +222,43 @@ void mean_chunk_kernel(GradArgs<PMAX> ga, int p, const float* acc, MeanOut<ODT> 
           } else {
             fold8<GDT>(s[1 + u], q[u]);
           }
+          __builtin_amdgcn_sched_barrier(0);  // fold in load order
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
 #pragma unroll
     for (int u = 0; u < kGroupsMax; ++u)
-      mo.put8(h + (g0 + static_cast<int64_t>(u) * kBlock) * kVec, lane16, s[u]);
+      mo.template put8<true>(h + (g0 + static_cast<int64_t>(u) * kBlock) * kVec, L, s[u]);
   }
   mean_rest<GDT, ODT>(gr, p, acc, mo, len, h, nvec, nfull * kFull, nfull, blockIdx.x, gridDim.x,
-                      lane16, lane32);
+                      L);
 }
 
-// The stored mean for smaller shards.  Workgroup-uniform bases, 8 elements
-// per lane, grid-stride over groups.
+// The stored mean for smaller shards, grid-stride over groups: full groups
+// in the full-group map, then the partial group, then the scalar head and
+// tail (block 0).
 template <int GDT, int ODT, int PMAX>
 __global__ __launch_bounds__(kBlock) void mean_kernel(GradArgs<PMAX> ga, int p, const float* acc,
                                                       MeanOut<ODT> mo, int64_t len, int head) {
   (void)ga;  // read through the kernel-argument segment, see kernarg_grads()
   const ArgGrads gr = kernarg_grads();
   const int tid = threadIdx.x;
-  const uint32_t lane16 = static_cast<uint32_t>(tid) * 16u;
-  const uint32_t lane32 = static_cast<uint32_t>(tid) * 32u;
+  const Lanes L = lanes();
   const int64_t h = head < len ? head : len;
   const int64_t nvec = (len - h) / kVec;
-  for (int64_t gb = static_cast<int64_t>(blockIdx.x) * kBlock; gb < nvec;
-       gb += static_cast<int64_t>(gridDim.x) * kBlock) {
-    if (gb + tid < nvec) {
-      const int64_t e0 = h + gb * kVec;
-      float g[kVec];
-      if (acc) {
-        load_acc8(acc, e0, lane32, g);
-        sum_ranks8<GDT, true>(gr, p, e0, lane16, g);
-      } else {
-        sum_ranks8<GDT>(gr, p, e0, lane16, g);
-      }
-      mo.put8(e0, lane16, g);
-    }
+  const int64_t nfg = nvec / kBlock, part = nvec % kBlock;
+  for (int64_t gi = blockIdx.x; gi < nfg; gi += gridDim.x) {
+    const int64_t e0 = h + gi * kGroup;
+    float g[kVec];
+    group_sums<GDT, true>(gr, p, acc, e0, L, g);
+    mo.template put8<true>(e0, L, g);
+  }
+  if (part > 0 && blockIdx.x == nfg % gridDim.x && tid < part) {
+    const int64_t e0 = h + nfg * kGroup;
+    float g[kVec];
+    group_sums<GDT, false>(gr, p, acc, e0, L, g);
+    mo.template put8<false>(e0, L, g);
   }
   if (blockIdx.x == 0) {
     const int64_t t0 = h + nvec * kVec;
@@ -248,7 +270,40 @@ __global__ __launch_bounds__(kBlock) void mean_kernel(GradArgs<PMAX> ga, int p, 
   }
 }
 
-// Adam + downcast from a stored fp32 gradient.
+// The update of the scalar head and tail elements from a stored gradient.
+template <int PDT, int FORM, bool PARAM>
+__device__ __forceinline__ void adam_scalars(const Consts& c, const float* gin, float* w,
+                                             float* m, float* v, uint16_t* par, int64_t len,
+                                             int64_t h, int64_t nvec) {
+  const int64_t t0 = h + nvec * kVec;
+  const int64_t nsc = h + (len - t0);
+  for (int64_t i = threadIdx.x; i < nsc; i += kBlock) {
+    const int64_t e = i < h ? i : t0 + (i - h);
+    float W = w[e], M = ld_state1<kUsesM<FORM>>(m + e), V = ld_state1<kUsesV<FORM>>(v + e);
+    adam1<FORM>(c, gin[e], W, M, V);
+    w[e] = W;
+    st_state1<kUsesM<FORM>>(m + e, M);
+    st_state1<kUsesV<FORM>>(v + e, V);
+    if constexpr (PARAM) par[e] = narrow1<PDT>(W);
+  }
+}
+
+// The update of one full group from a stored gradient (state and gradient
+// loads issued together).
+template <int PDT, int FORM, bool PARAM>
+__device__ __forceinline__ void adam_group(const Consts& c, const Lanes& L, const float* gin,
+                                           float* w, float* m, float* v, uint16_t* par,
+                                           int64_t e0) {
+  float g[kVec];
+  ld_f8(gin + e0, L, g);
+  const GroupState q = load_group<FORM>(L, w, m, v, e0);
+  apply_group<PDT, FORM, false, PARAM>(c, L, q, g, w, m, v, par, e0);
+}
+
+// Adam + downcast from a stored fp32 gradient, for smaller shards: pairs of
+// full groups grid-stride (both groups' loads in flight together), then the
+// odd full group and the partial group as two more items, then the scalars
+// (block 0).
 template <int PDT, int FORM, bool PARAM>
 __global__ __launch_bounds__(kBlock) void adam_kernel(const float* __restrict__ gin,
                                                       float* __restrict__ w,
@@ -257,60 +312,41 @@ __global__ __launch_bounds__(kBlock) void adam_kernel(const float* __restrict__ 
                                                       uint16_t* __restrict__ par, int64_t len,
                                                       int head, Consts c) {
   const int tid = threadIdx.x;
-  const uint32_t lane16 = static_cast<uint32_t>(tid) * 16u;
-  const uint32_t lane32 = static_cast<uint32_t>(tid) * 32u;
+  const Lanes L = lanes();
   const int64_t h = head < len ? head : len;
   const int64_t nvec = (len - h) / kVec;
-  // Two vectors per lane per iteration, both vectors' loads in flight
-  // together (14% faster than one on the 117M-element shard); the block whose
-  // turn comes after the last whole pair takes the partial pair.
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kBlock * 2;
-  int64_t gb = static_cast<int64_t>(blockIdx.x) * kBlock * 2;
-  for (; gb + 2 * kBlock <= nvec; gb += stride) {
-    const int64_t e0 = h + gb * kVec;
-    const int64_t e1 = e0 + static_cast<int64_t>(kBlock) * kVec;
-    const f32x4 a0 = ld_f32x4(gin + e0, lane32), a1 = ld_f32x4(gin + e0, lane32 + 16);
-    const f32x4 b0 = ld_f32x4(gin + e1, lane32), b1 = ld_f32x4(gin + e1, lane32 + 16);
-    const float ga[kVec] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-    const float gb2[kVec] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-    adam8x2<PDT, FORM, false, PARAM>(c, ga, gb2, w, m, v, par, e0, e1, lane16, lane32);
+  const int64_t nfg = nvec / kBlock, part = nvec % kBlock;
+  const int64_t npairs = nfg / 2;
+  for (int64_t i = blockIdx.x; i < npairs; i += gridDim.x) {
+    const int64_t e0 = h + 2 * i * kGroup, e1 = e0 + kGroup;
+    float a[kVec], b[kVec];
+    ld_f8(gin + e0, L, a);
+    ld_f8(gin + e1, L, b);
+    adam8x2<PDT, FORM, false, PARAM>(c, a, b, w, m, v, par, e0, e1, L);
   }
-  for (; gb < nvec; gb += kBlock) {
-    if (gb + tid < nvec) {
-      const int64_t e0 = h + gb * kVec;
-      const f32x4 a = ld_f32x4(gin + e0, lane32), b = ld_f32x4(gin + e0, lane32 + 16);
-      const float g[kVec] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-      adam8<PDT, FORM, PARAM>(c, g, w, m, v, par, e0, lane16, lane32);
-    }
+  if ((nfg & 1) && blockIdx.x == npairs % gridDim.x)
+    adam_group<PDT, FORM, PARAM>(c, L, gin, w, m, v, par, h + (nfg - 1) * kGroup);
+  if (part > 0 && blockIdx.x == (npairs + 1) % gridDim.x && tid < part) {
+    const int64_t e0 = h + nfg * kGroup;
+    const f32x4 a = ld_f32x4(gin + e0, L.c32), b = ld_f32x4(gin + e0, L.c32 + 16);
+    const float g[kVec] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    adam8<PDT, FORM, PARAM>(c, g, w, m, v, par, e0, L);
   }
-  if (blockIdx.x == 0) {
-    const int64_t t0 = h + nvec * kVec;
-    const int64_t nsc = h + (len - t0);
-    for (int64_t i = tid; i < nsc; i += kBlock) {
-      const int64_t e = i < h ? i : t0 + (i - h);
-      float W = w[e], M = ld_state1<kUsesM<FORM>>(m + e), V = ld_state1<kUsesV<FORM>>(v + e);
-      adam1<FORM>(c, gin[e], W, M, V);
-      w[e] = W;
-      st_state1<kUsesM<FORM>>(m + e, M);
-      st_state1<kUsesV<FORM>>(v + e, V);
-      if constexpr (PARAM) par[e] = narrow1<PDT>(W);
-    }
-  }
+  if (blockIdx.x == 0) adam_scalars<PDT, FORM, PARAM>(c, gin, w, m, v, par, len, h, nvec);
 }
 
 // The update from a stored gradient (the unfused second half) for shards
 // with whole chunks for at least half the CUs, in the shape of fused_kernel's
 // update phase: whole chunks round-robin over one workgroup per CU (one wave
-// per SIMD), the chunk's groups one after another.  16% faster than
-// adam_kernel on the 117M-element shard.
+// per SIMD), the chunk's groups one after another; then the remaining full
+// groups grid-stride, the partial group and the scalars.
 template <int PDT, int FORM, bool PARAM>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void adam_chunk_kernel(const float* __restrict__ gin, float* __restrict__ w,
                        float* __restrict__ m, float* __restrict__ v,
                        uint16_t* __restrict__ par, int64_t len, int head, Consts c) {
   const int tid = threadIdx.x;
-  const uint32_t lane16 = static_cast<uint32_t>(tid) * 16u;
-  const uint32_t lane32 = static_cast<uint32_t>(tid) * 32u;
+  const Lanes L = lanes();
   const int64_t h = head < len ? head : len;
   const int64_t nvec = (len - h) / kVec;
   constexpr int64_t kFull = static_cast<int64_t>(kBlock) * kGroupsMax;
@@ -318,36 +354,20 @@ void adam_chunk_kernel(const float* __restrict__ gin, float* __restrict__ w,
   for (int64_t ch = blockIdx.x; ch < nfull; ch += gridDim.x) {
     const int64_t g0 = ch * kFull;
 #pragma unroll
-    for (int u = 0; u < kGroupsMax; ++u) {
-      const int64_t e0 = h + (g0 + static_cast<int64_t>(u) * kBlock) * kVec;
-      const f32x4 a = ld_f32x4(gin + e0, lane32), b = ld_f32x4(gin + e0, lane32 + 16);
-      const float g[kVec] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-      adam8<PDT, FORM, PARAM>(c, g, w, m, v, par, e0, lane16, lane32);
-    }
+    for (int u = 0; u < kGroupsMax; ++u)
+      adam_group<PDT, FORM, PARAM>(c, L, gin, w, m, v, par,
+                                   h + (g0 + static_cast<int64_t>(u) * kBlock) * kVec);
   }
-  // the vectors after the whole chunks (fewer than one chunk), grid-stride
-  for (int64_t gb = nfull * kFull + static_cast<int64_t>(blockIdx.x) * kBlock; gb < nvec;
-       gb += static_cast<int64_t>(gridDim.x) * kBlock) {
-    if (gb + tid < nvec) {
-      const int64_t e0 = h + gb * kVec;
-      const f32x4 a = ld_f32x4(gin + e0, lane32), b = ld_f32x4(gin + e0, lane32 + 16);
-      const float g[kVec] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-      adam8<PDT, FORM, PARAM>(c, g, w, m, v, par, e0, lane16, lane32);
-    }
+  const int64_t nfg = nvec / kBlock, part = nvec % kBlock;
+  for (int64_t gi = nfull * kGroupsMax + blockIdx.x; gi < nfg; gi += gridDim.x)
+    adam_group<PDT, FORM, PARAM>(c, L, gin, w, m, v, par, h + gi * kGroup);
+  if (part > 0 && blockIdx.x == nfg % gridDim.x && tid < part) {
+    const int64_t e0 = h + nfg * kGroup;
+    const f32x4 a = ld_f32x4(gin + e0, L.c32), b = ld_f32x4(gin + e0, L.c32 + 16);
+    const float g[kVec] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    adam8<PDT, FORM, PARAM>(c, g, w, m, v, par, e0, L);
   }
-  if (blockIdx.x == 0) {
-    const int64_t t0 = h + nvec * kVec;
-    const int64_t nsc = h + (len - t0);
-    for (int64_t i = tid; i < nsc; i += kBlock) {
-      const int64_t e = i < h ? i : t0 + (i - h);
-      float W = w[e], M = ld_state1<kUsesM<FORM>>(m + e), V = ld_state1<kUsesV<FORM>>(v + e);
-      adam1<FORM>(c, gin[e], W, M, V);
-      w[e] = W;
-      st_state1<kUsesM<FORM>>(m + e, M);
-      st_state1<kUsesV<FORM>>(v + e, V);
-      if constexpr (PARAM) par[e] = narrow1<PDT>(W);
-    }
-  }
+  if (blockIdx.x == 0) adam_scalars<PDT, FORM, PARAM>(c, gin, w, m, v, par, len, h, nvec);
 }
 
 }  // namespace

@@ -615,7 +615,9 @@ def ceiling(args):
     sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
     mixes = [("read", 0, None), ("copy", 1, None), ("mix_10_1", 4, 154), ("mix_22_7", 3, 58),
              ("mix_2_1", 2, 42), ("phased_read", 5, None), ("phased_copy", 6, None),
-             ("phased_10_1", 9, 154), ("phased_22_7", 8, 58), ("phased_2_1", 7, 42)]
+             ("phased_10_1", 9, 154), ("phased_22_7", 8, 58), ("phased_2_1", 7, 42),
+             ("read_1x16", 10, None), ("read_2x8", 11, None), ("read_4x8", 12, None),
+             ("read_8x8", 13, None), ("read_1x32", 14, None)]
     out = {}
     for name, mix, bpe in mixes:
         nr, nw = C.c_int32(), C.c_int32()

@@ -28,7 +28,10 @@ extern "C" {
 enum {
   ZSP_READ8 = 0, ZSP_COPY = 1, ZSP_MIX_2_1 = 2, ZSP_MIX_22_7 = 3, ZSP_MIX_10_1 = 4,
   ZSP_PHASED_READ8 = 5, ZSP_PHASED_COPY = 6, ZSP_PHASED_2_1 = 7, ZSP_PHASED_22_7 = 8,
-  ZSP_PHASED_10_1 = 9
+  ZSP_PHASED_10_1 = 9,
+  /* more pure-read shapes: read streams x 16-byte loads in flight per lane
+   * and stream (ZSP_READ8 is 8 x 4) */
+  ZSP_READ1_U16 = 10, ZSP_READ2_U8 = 11, ZSP_READ4_U8 = 12, ZSP_READ8_U8 = 13, ZSP_READ1_U32 = 14
 };
 
 /* Read and write streams of a mix; 0 on success, 1 on a bad mix. */
