@@ -30,7 +30,7 @@
 //    dealt to the workgroups that got one chunk fewer, and is read with the
 //    ranks batched, so the workgroups finish together.  Shards under half a
 //    chunk per CU get no whole chunk: small_kernel deals their pieces over
-//    four workgroups per CU instead.
+//    three workgroups per CU instead.
 //  - No MFMA and no LDS on the single-tensor path (nothing is reused); the
 //    multi-tensor path stages one chunk's descriptors in LDS.
 // Arithmetic (rank-order fp32 mean, Adam moments, bias correction, update,
@@ -199,7 +199,7 @@ struct LdsGrads {
 
 constexpr int kRankBatch = 8;
 // Waves per SIMD (workgroups per CU) of the small-shard kernel.
-constexpr int kSmallWaves = 4;
+constexpr int kSmallWaves = 3;
 
 // ---- the lane maps -------------------------------------------------------
 // Byte offsets of one lane inside a group, added to a workgroup-uniform base
@@ -262,6 +262,38 @@ template <int DT>
 __device__ __forceinline__ void st_h8(uint16_t* base, const Lanes& L, const float (&x)[kVec]) {
   st_u16x4(base, L.q16, u32x2{narrow2<DT>(x[0], x[1]), narrow2<DT>(x[2], x[3])});
   st_u16x4(base, L.q16 + 512u, u32x2{narrow2<DT>(x[4], x[5]), narrow2<DT>(x[6], x[7])});
+}
+
+// Whole-line fp32 stores from the contiguous map.  Lane l of a wave holds 8
+// consecutive values, its low quad X_l and high quad Y_l, 32 bytes at 32 l.
+// Stored as they lie, each store instruction would write half of every
+// 128-byte line it touches.  v_permlane32_swap trades lanes 32..63's X for
+// lanes 0..31's Y, so the first instruction writes the wave's first KiB (X_l
+// and Y_l of lanes 0..31) and the second its second KiB.  All 64 lanes must
+// be active.
+struct SwapOffs {
+  uint32_t a, b;  // byte offsets of this lane's two stores
+};
+__device__ __forceinline__ SwapOffs swap_offs(uint32_t c32) {
+  const bool hi = (threadIdx.x & 32u) != 0;
+  // lane l >= 32 stores Y_{l-32} at 32 (l - 32) + 16, then its own Y_l;
+  // lane l < 32 its own X_l, then X_{l+32} at 32 (l + 32)
+  return SwapOffs{hi ? c32 - 1008u : c32, hi ? c32 + 16u : c32 + 1024u};
+}
+__device__ __forceinline__ void st_f32x8_lines(float* base, const SwapOffs& o,
+                                               const float (&x)[kVec]) {
+  f32x4 a, b;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    // lanes 0..31 keep x[d] in a and receive lanes 32..63's x[d] in b;
+    // lanes 32..63 receive lanes 0..31's x[4 + d] in a and keep x[4 + d] in b
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[d]),
+                                                    __float_as_uint(x[4 + d]), false, false);
+    a[d] = __uint_as_float(r[0]);
+    b[d] = __uint_as_float(r[1]);
+  }
+  st_f32x4(base, o.a, a);
+  st_f32x4(base, o.b, b);
 }
 
 // Which optimizer state a form reads and writes: Adam both moments, momentum
@@ -662,8 +694,8 @@ __device__ __forceinline__ RestPlan rest_plan(int64_t nvec, int64_t left0, int64
   return r;
 }
 
-// FULL picks the lane map of full groups (the contiguous one measured faster
-// in the four-workgroup small-shard kernel).
+// FULL picks the lane map of full groups: the full-group map, or the
+// contiguous one (8 consecutive elements per lane).
 template <int GDT, int PDT, int FORM, int MAXB = 16, bool FULL = true, class Grads>
 __device__ __forceinline__ void fused_rest(const Grads& gr, int p, float* __restrict__ w,
                                            float* __restrict__ m, float* __restrict__ v,

@@ -23,10 +23,12 @@ namespace {
 // full-group map makes each phase faster alone (reads 2.33 -> 2.29 ms,
 // update 0.67 -> 0.60 ms) but the step slower (2.78 -> 2.85-2.89 ms): its
 // dense full-line store bursts overlap worse with other CUs' read phases.
-// The price of this map is that each store instruction writes half of every
-// cache line it touches, and about 5% of the written bytes are repeated.
-// The loop is also sensitive to its exact shape: scheduling barriers that
-// force each load's issue order made it 9% slower (3.03 ms).
+// Stored as they lie, this map's fp32 values would fill half of every cache
+// line per store instruction (5% of the written bytes were repeated); a
+// cross-lane swap before the stores (st_f32x8_lines) makes each instruction
+// write whole lines, and the step 1.4% faster.  The loop is sensitive to its
+// exact shape: scheduling barriers that force each load's issue order made
+// it 9% slower (3.03 ms), and swapping the state loads the same way 6%.
 template <int GDT, int PDT, int FORM, int PMAX>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fused_kernel(GradArgs<PMAX> ga, int p, float* __restrict__ w, float* __restrict__ m,
@@ -38,6 +40,7 @@ void fused_kernel(GradArgs<PMAX> ga, int p, float* __restrict__ w, float* __rest
   const int64_t nvec = (len - h) / kVec;
   const uint32_t lane16 = threadIdx.x * 16u;
   const uint32_t lane32 = threadIdx.x * 32u;
+  const SwapOffs so = swap_offs(lane32);
   constexpr int64_t kFull = static_cast<int64_t>(kBlock) * kGroupsMax;
   const int64_t nfull = whole_chunks(nvec / kFull, gridDim.x);
   for (int64_t ch = blockIdx.x; ch < nfull; ch += gridDim.x) {
@@ -110,12 +113,10 @@ void fused_kernel(GradArgs<PMAX> ga, int p, float* __restrict__ w, float* __rest
       float V[kVec] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
       for (int j = 0; j < kVec; ++j) adam1<FORM>(c, s[u][j] / c.PF, W[j], M[j], V[j]);
-      st_f32x4(wb, lane32, f32x4{W[0], W[1], W[2], W[3]});
-      st_f32x4(wb, lane32 + 16, f32x4{W[4], W[5], W[6], W[7]});
-      st_state<kUsesM<FORM>>(mb, lane32, f32x4{M[0], M[1], M[2], M[3]});
-      st_state<kUsesM<FORM>>(mb, lane32 + 16, f32x4{M[4], M[5], M[6], M[7]});
-      st_state<kUsesV<FORM>>(vb, lane32, f32x4{V[0], V[1], V[2], V[3]});
-      st_state<kUsesV<FORM>>(vb, lane32 + 16, f32x4{V[4], V[5], V[6], V[7]});
+      // state stores as whole lines (1 KiB per wave instruction)
+      st_f32x8_lines(wb, so, W);
+      if constexpr (kUsesM<FORM>) st_f32x8_lines(mb, so, M);
+      if constexpr (kUsesV<FORM>) st_f32x8_lines(vb, so, V);
       st_u16x8(par + e0, lane16,
                u32x4{narrow2<PDT>(W[0], W[1]), narrow2<PDT>(W[2], W[3]),
                      narrow2<PDT>(W[4], W[5]), narrow2<PDT>(W[6], W[7])});
@@ -127,10 +128,12 @@ void fused_kernel(GradArgs<PMAX> ga, int p, float* __restrict__ w, float* __rest
 
 // Single-tensor fused step for shards under half a whole chunk per CU, where
 // fused_kernel would run no whole chunk at all: the same pieces of two
-// groups, dealt over four workgroups per CU (four waves per SIMD), in the
-// full-group lane map with rank batches of 4.  On the 16-rank,
-// 6.25M-element shards: 64.4 us against 66.6 (contiguous map, batches of 8)
-// and 68.8 (contiguous, 4); four workgroups per CU were 4% faster than one.
+// groups, dealt over three workgroups per CU (three waves per SIMD, 168
+// registers: no spills), in the full-group lane map with rank batches of 4.
+// On the 16-rank, 6.25M-element shards: 63.2 us, against 63.8 with four
+// workgroups per CU (128 registers, 5 spilled), 66.6 with the contiguous map
+// and batches of 8, 68.8 with the contiguous map and batches of 4; one
+// workgroup per CU was 4% slower.
 template <int GDT, int PDT, int FORM, int PMAX>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kSmallWaves)))
 void small_kernel(GradArgs<PMAX> ga, int p, float* __restrict__ w, float* __restrict__ m,
