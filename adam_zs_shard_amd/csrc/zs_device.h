@@ -12,7 +12,10 @@
 //    8-byte access of a 16-bit array (gradients, working copy) covers 512
 //    contiguous bytes per wave, each 16-byte access of an fp32 array (w, m,
 //    v) 1 KiB, so no store instruction leaves a cache line half written.  The
-//    last, partial group of a range keeps 8 consecutive elements per lane.
+//    last, partial group of a range keeps 8 consecutive elements per lane,
+//    and so do the whole chunks of the single-tensor fused kernel (one
+//    16-byte gradient load per rank and group), whose fp32 stores are made
+//    whole-line by a cross-lane swap (st_f32x8_lines).
 //  - Gradient reads are rank-major: for each rank in turn a wave issues its
 //    first group's loads, uses them, then the other 27 groups' loads of the
 //    chunk back to back (scheduling barriers stop the compiler from sinking
@@ -344,21 +347,6 @@ __device__ __forceinline__ void fold8(float (&acc)[kVec], const G8& q) {
   acc[4] = acc[4] + widen_lo<GDT>(q.b.x); acc[5] = acc[5] + widen_hi<GDT>(q.b.x);
   acc[6] = acc[6] + widen_lo<GDT>(q.b.y); acc[7] = acc[7] + widen_hi<GDT>(q.b.y);
 }
-// One quad (4 consecutive 16-bit values) into acc[j0 .. j0+3].
-__device__ __forceinline__ u32x2 ld_quad(const uint16_t* base, uint32_t off) {
-  return __builtin_nontemporal_load(
-      reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(base) + off));
-}
-template <int GDT>
-__device__ __forceinline__ void init4(float (&acc)[kVec], int j0, const u32x2& q) {
-  acc[j0] = widen_lo<GDT>(q.x); acc[j0 + 1] = widen_hi<GDT>(q.x);
-  acc[j0 + 2] = widen_lo<GDT>(q.y); acc[j0 + 3] = widen_hi<GDT>(q.y);
-}
-template <int GDT>
-__device__ __forceinline__ void fold4(float (&acc)[kVec], int j0, const u32x2& q) {
-  acc[j0] = acc[j0] + widen_lo<GDT>(q.x); acc[j0 + 1] = acc[j0 + 1] + widen_hi<GDT>(q.x);
-  acc[j0 + 2] = acc[j0 + 2] + widen_lo<GDT>(q.y); acc[j0 + 3] = acc[j0 + 3] + widen_hi<GDT>(q.y);
-}
 // The partial group (u32x4): 8 consecutive elements.
 template <int GDT>
 __device__ __forceinline__ void init8(float (&acc)[kVec], const u32x4& q) {
@@ -472,8 +460,8 @@ __device__ __forceinline__ void fold_batch2(const Grads& gr, int r0, int64_t e0,
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// MAXB caps the rank batch (16, 8 or 4): the small-shard kernel, with four
-// waves per SIMD, takes 4.
+// MAXB caps the rank batch (16, 8 or 4): the small-shard kernel, with three
+// waves per SIMD, takes 4; the chunk table's rest 8.
 template <int GDT, int MAXB = 16, bool FULL = true, bool CONT = false, class Grads>
 __device__ __forceinline__ void sum_ranks8x2(const Grads& gr, int p, int64_t e0, int64_t e1,
                                              const Lanes& L, float (&a)[kVec],
@@ -604,62 +592,17 @@ __device__ __forceinline__ void adam8(const Consts& c, const float (&x)[kVec], f
                    narrow2<PDT>(W[6], W[7])});
 }
 
-// Two groups (either map): both groups' state loads issued together, then
-// the arithmetic and stores of each.
-template <int PDT, int FORM, bool DIVIDE = true, bool PARAM = true, bool FULL = true>
+// Two full groups: both groups' state loads issued together, then the
+// arithmetic and stores of each.
+template <int PDT, int FORM, bool DIVIDE = true, bool PARAM = true>
 __device__ __forceinline__ void adam8x2(const Consts& c, const float (&a)[kVec],
                                         const float (&b)[kVec], float* w, float* m, float* v,
                                         uint16_t* par, int64_t e0, int64_t e1, const Lanes& L) {
-  if constexpr (FULL) {
-    const GroupState qa = load_group<FORM>(L, w, m, v, e0);
-    const GroupState qb = load_group<FORM>(L, w, m, v, e1);
-    __builtin_amdgcn_sched_barrier(0);
-    apply_group<PDT, FORM, DIVIDE, PARAM>(c, L, qa, a, w, m, v, par, e0);
-    apply_group<PDT, FORM, DIVIDE, PARAM>(c, L, qb, b, w, m, v, par, e1);
-  } else {
-    const uint32_t lane16 = L.c16, lane32 = L.c32;
-    f32x4 S[2][6];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int64_t e = q == 0 ? e0 : e1;
-      S[q][0] = ld_f32x4(w + e, lane32);
-      S[q][1] = ld_f32x4(w + e, lane32 + 16);
-      S[q][2] = ld_state<kUsesM<FORM>>(m + e, lane32);
-      S[q][3] = ld_state<kUsesM<FORM>>(m + e, lane32 + 16);
-      S[q][4] = ld_state<kUsesV<FORM>>(v + e, lane32);
-      S[q][5] = ld_state<kUsesV<FORM>>(v + e, lane32 + 16);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int64_t e = q == 0 ? e0 : e1;
-      const float(&x)[kVec] = q == 0 ? a : b;
-      float W[kVec] = {S[q][0].x, S[q][0].y, S[q][0].z, S[q][0].w,
-                       S[q][1].x, S[q][1].y, S[q][1].z, S[q][1].w};
-      float M[kVec] = {S[q][2].x, S[q][2].y, S[q][2].z, S[q][2].w,
-                       S[q][3].x, S[q][3].y, S[q][3].z, S[q][3].w};
-      float V[kVec] = {S[q][4].x, S[q][4].y, S[q][4].z, S[q][4].w,
-                       S[q][5].x, S[q][5].y, S[q][5].z, S[q][5].w};
-#pragma unroll
-      for (int j = 0; j < kVec; ++j) {
-        if constexpr (DIVIDE) {
-          adam1<FORM>(c, x[j] / c.PF, W[j], M[j], V[j]);
-        } else {
-          adam1<FORM>(c, x[j], W[j], M[j], V[j]);
-        }
-      }
-      st_f32x4(w + e, lane32, f32x4{W[0], W[1], W[2], W[3]});
-      st_f32x4(w + e, lane32 + 16, f32x4{W[4], W[5], W[6], W[7]});
-      st_state<kUsesM<FORM>>(m + e, lane32, f32x4{M[0], M[1], M[2], M[3]});
-      st_state<kUsesM<FORM>>(m + e, lane32 + 16, f32x4{M[4], M[5], M[6], M[7]});
-      st_state<kUsesV<FORM>>(v + e, lane32, f32x4{V[0], V[1], V[2], V[3]});
-      st_state<kUsesV<FORM>>(v + e, lane32 + 16, f32x4{V[4], V[5], V[6], V[7]});
-      if constexpr (PARAM)
-        st_u16x8(par + e, lane16,
-                 u32x4{narrow2<PDT>(W[0], W[1]), narrow2<PDT>(W[2], W[3]),
-                       narrow2<PDT>(W[4], W[5]), narrow2<PDT>(W[6], W[7])});
-    }
-  }
+  const GroupState qa = load_group<FORM>(L, w, m, v, e0);
+  const GroupState qb = load_group<FORM>(L, w, m, v, e1);
+  __builtin_amdgcn_sched_barrier(0);
+  apply_group<PDT, FORM, DIVIDE, PARAM>(c, L, qa, a, w, m, v, par, e0);
+  apply_group<PDT, FORM, DIVIDE, PARAM>(c, L, qb, b, w, m, v, par, e1);
 }
 
 // ---- the rest of a range ---------------------------------------------------
@@ -694,9 +637,9 @@ __device__ __forceinline__ RestPlan rest_plan(int64_t nvec, int64_t left0, int64
   return r;
 }
 
-// FULL picks the lane map of full groups: the full-group map, or the
-// contiguous one (8 consecutive elements per lane).
-template <int GDT, int PDT, int FORM, int MAXB = 16, bool FULL = true, class Grads>
+// Full groups in the full-group lane map, the partial group in the
+// contiguous one; MAXB caps the rank batch.
+template <int GDT, int PDT, int FORM, int MAXB = 16, class Grads>
 __device__ __forceinline__ void fused_rest(const Grads& gr, int p, float* __restrict__ w,
                                            float* __restrict__ m, float* __restrict__ v,
                                            uint16_t* __restrict__ par, int64_t len, int64_t h,
@@ -710,18 +653,14 @@ __device__ __forceinline__ void fused_rest(const Grads& gr, int p, float* __rest
       const int64_t e0 = h + (R.first_full + 2 * i * kBlock) * kVec;
       const int64_t e1 = e0 + kGroup;
       float a[kVec], b[kVec];
-      sum_ranks8x2<GDT, MAXB, FULL>(gr, p, e0, e1, L, a, b);
-      adam8x2<PDT, FORM, true, true, FULL>(c, a, b, w, m, v, par, e0, e1, L);
+      sum_ranks8x2<GDT, MAXB>(gr, p, e0, e1, L, a, b);
+      adam8x2<PDT, FORM>(c, a, b, w, m, v, par, e0, e1, L);
     } else if (i == R.npairs && (R.nfg & 1)) {
       const int64_t e0 = h + (R.first_full + 2 * R.npairs * kBlock) * kVec;
       float g[kVec];
-      sum_ranks8<GDT, FULL, false, MAXB>(gr, p, e0, L, g);
-      if constexpr (FULL) {
-        const GroupState q = load_group<FORM>(L, w, m, v, e0);
-        apply_group<PDT, FORM>(c, L, q, g, w, m, v, par, e0);
-      } else {
-        adam8<PDT, FORM, true, true>(c, g, w, m, v, par, e0, L);
-      }
+      sum_ranks8<GDT, true, false, MAXB>(gr, p, e0, L, g);
+      const GroupState q = load_group<FORM>(L, w, m, v, e0);
+      apply_group<PDT, FORM>(c, L, q, g, w, m, v, par, e0);
     } else if (tid < R.part) {
       const int64_t e0 = h + (R.first_full + R.nfg * kBlock) * kVec;
       float g[kVec];

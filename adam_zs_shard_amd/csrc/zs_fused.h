@@ -143,8 +143,8 @@ void small_kernel(GradArgs<PMAX> ga, int p, float* __restrict__ w, float* __rest
   const ArgGrads gr = rank_grads(rank_table);
   const int64_t h = head < len ? head : len;
   const int64_t nvec = (len - h) / kVec;
-  fused_rest<GDT, PDT, FORM, 4, true>(gr, p, w, m, v, par, len, h, nvec, 0, 0, c, blockIdx.x,
-                                       gridDim.x, lanes());
+  fused_rest<GDT, PDT, FORM, 4>(gr, p, w, m, v, par, len, h, nvec, 0, 0, c, blockIdx.x,
+                                gridDim.x, lanes());
 }
 
 }  // namespace
