@@ -54,10 +54,10 @@ struct Events {
     for (hipEvent_t e : ev)
       if (e) (void)hipEventDestroy(e);
   }
-  hipError_t make(size_t n) {
+  hipError_t make(size_t n, unsigned flags = hipEventDisableTiming) {
     ev.assign(n, nullptr);
     for (auto& e : ev) {
-      const hipError_t r = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+      const hipError_t r = hipEventCreateWithFlags(&e, flags);
       if (r != hipSuccess) return r;
     }
     return hipSuccess;
@@ -147,7 +147,10 @@ extern "C" zs_status zs_offload_step(const zs_offload_args* a, const zs_adam_hpa
   const hipStream_t hs = static_cast<hipStream_t>(a->h2d_stream);
   Events mean_done, copied;
   hipError_t err = mean_done.make(static_cast<size_t>(nb));
-  if (err == hipSuccess) err = copied.make(static_cast<size_t>(nb));
+  // the host waits on `copied`: blocking events, so the waiting thread sleeps
+  // instead of spinning on a core the update's workers need
+  if (err == hipSuccess)
+    err = copied.make(static_cast<size_t>(nb), hipEventDisableTiming | hipEventBlockingSync);
   auto fail = [](hipError_t x) { return static_cast<zs_status>(zs::hip_status(x)); };
   if (err != hipSuccess) return fail(err);
 
