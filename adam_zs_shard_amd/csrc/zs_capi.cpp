@@ -111,6 +111,7 @@ const char* zs_status_string(int32_t status) {
     case ZS_ERR_CAPACITY: return "ZS_ERR_CAPACITY";
     case ZS_ERR_HIP: return "ZS_ERR_HIP";
     case ZS_ERR_UNSUPPORTED: return "ZS_ERR_UNSUPPORTED";
+    case ZS_ERR_RESOURCE: return "ZS_ERR_RESOURCE";
     default: return "ZS_ERR_UNKNOWN";
   }
 }
@@ -234,9 +235,13 @@ zs_status fused_impl(const zs_shard_args* a, bool use_static) {
 
 extern "C" {
 
-zs_status zs_fused_shard_step(const zs_shard_args* a) { return fused_impl(a, false); }
+zs_status zs_fused_shard_step(const zs_shard_args* a) {
+  return zs::guard([&] { return fused_impl(a, false); });
+}
 
-zs_status zs_fused_shard_step_static(const zs_shard_args* a) { return fused_impl(a, true); }
+zs_status zs_fused_shard_step_static(const zs_shard_args* a) {
+  return zs::guard([&] { return fused_impl(a, true); });
+}
 
 }  // extern "C"
 
@@ -300,7 +305,8 @@ extern "C" {
 zs_status zs_reduce_scatter_mean_local(const void* const* grads, int32_t grad_dtype,
                                        int64_t grad_base, int64_t n, int32_t p, int32_t k,
                                        float* g_out, void* stream) {
-  return mean_impl(grads, grad_dtype, grad_base, n, p, k, g_out, 0, nullptr, stream);
+  return zs::guard(
+      [&] { return mean_impl(grads, grad_dtype, grad_base, n, p, k, g_out, 0, nullptr, stream); });
 }
 
 zs_status zs_reduce_scatter_mean_local16(const void* const* grads, int32_t grad_dtype,
@@ -308,12 +314,14 @@ zs_status zs_reduce_scatter_mean_local16(const void* const* grads, int32_t grad_
                                          void* g_out, int32_t out_dtype, float* partial,
                                          void* stream) {
   if (!dtype_ok(out_dtype)) return ZS_ERR_DTYPE;
-  return mean_impl(grads, grad_dtype, grad_base, n, p, k, g_out, out_dtype, partial, stream);
+  return zs::guard([&] {
+    return mean_impl(grads, grad_dtype, grad_base, n, p, k, g_out, out_dtype, partial, stream);
+  });
 }
 
-zs_status zs_adam_step(const float* g, float* w, float* m, float* v, void* param,
-                       int32_t param_dtype, int64_t len, const zs_adam_hparams* hp,
-                       void* stream) {
+static zs_status adam_step_body(const float* g, float* w, float* m, float* v, void* param,
+                                int32_t param_dtype, int64_t len, const zs_adam_hparams* hp,
+                                void* stream) {
   if (len < 0) return ZS_ERR_ARG;
   if (len > kMaxN) return ZS_ERR_RANGE;
   if (param && !dtype_ok(param_dtype)) return ZS_ERR_DTYPE;
@@ -359,6 +367,13 @@ zs_status zs_adam_step(const float* g, float* w, float* m, float* v, void* param
   const hipError_t err = zs::launch_adam(L);
   if (err != hipSuccess) return hip_fail(err);
   return ZS_OK;
+}
+
+zs_status zs_adam_step(const float* g, float* w, float* m, float* v, void* param,
+                       int32_t param_dtype, int64_t len, const zs_adam_hparams* hp,
+                       void* stream) {
+  return zs::guard(
+      [&] { return adam_step_body(g, w, m, v, param, param_dtype, len, hp, stream); });
 }
 
 // ---------------------------------------------------------------- multi
@@ -500,9 +515,10 @@ size_t zs_mt_workspace_bytes(int32_t npieces, int64_t nchunks, int32_t p) {
   return zs::mt_layout(npieces, nchunks, p).total;
 }
 
-zs_status zs_mt_upload(const zs_piece* pieces, const zs_piece_ptrs* ptrs, int32_t npieces,
-                       int32_t p, int32_t grad_dtype, int32_t param_dtype, int64_t chunk_elems,
-                       void* workspace, size_t ws_bytes, void* stream, zs_mt_table* table) {
+static zs_status mt_upload_body(const zs_piece* pieces, const zs_piece_ptrs* ptrs,
+                                int32_t npieces, int32_t p, int32_t grad_dtype,
+                                int32_t param_dtype, int64_t chunk_elems, void* workspace,
+                                size_t ws_bytes, void* stream, zs_mt_table* table) {
   if (!table || !workspace || (npieces > 0 && (!pieces || !ptrs))) return ZS_ERR_NULL;
   if (p < 1 || p > ZS_MAX_P || npieces < 0 || chunk_elems < zs::kVec ||
       chunk_elems % zs::kVec != 0)
@@ -604,6 +620,15 @@ zs_status zs_mt_upload(const zs_piece* pieces, const zs_piece_ptrs* ptrs, int32_
   return ZS_OK;
 }
 
+zs_status zs_mt_upload(const zs_piece* pieces, const zs_piece_ptrs* ptrs, int32_t npieces,
+                       int32_t p, int32_t grad_dtype, int32_t param_dtype, int64_t chunk_elems,
+                       void* workspace, size_t ws_bytes, void* stream, zs_mt_table* table) {
+  return zs::guard([&] {
+    return mt_upload_body(pieces, ptrs, npieces, p, grad_dtype, param_dtype, chunk_elems,
+                          workspace, ws_bytes, stream, table);
+  });
+}
+
 }  // extern "C"
 
 namespace {
@@ -645,7 +670,8 @@ zs_status launch_table(const zs_mt_table* t, int32_t form, const zs::Consts& c,
 
 zs_status check_steps(const zs_step_table* st) {
   if (!st || !st->dev) return ZS_ERR_NULL;
-  if (st->nsteps < 1 || st->p < 1 || st->p > ZS_MAX_P || st->form < ZS_ADAM_STANDARD ||
+  if (st->nsteps < 1 || st->nsteps > ZS_MAX_TABLE_STEPS || st->p < 1 || st->p > ZS_MAX_P ||
+      st->form < ZS_ADAM_STANDARD ||
       st->form > ZS_SGD_MOMENTUM)
     return ZS_ERR_ARG;
   return ZS_OK;
@@ -663,16 +689,17 @@ zs_status zs_fused_shard_step_multi(const zs_mt_table* t, const zs_adam_hparams*
 }
 
 size_t zs_step_table_bytes(int32_t nsteps) {
-  if (nsteps < 1) return 0;
+  if (nsteps < 1 || nsteps > ZS_MAX_TABLE_STEPS) return 0;
   const size_t b = zs::kStepTableHead + sizeof(zs::Consts) * static_cast<size_t>(nsteps);
   return (b + 255u) & ~static_cast<size_t>(255u);
 }
 
-zs_status zs_step_table_init(const zs_adam_hparams* hp, int32_t p, int32_t nsteps, void* dev,
-                             size_t bytes, void* stream, zs_step_table* table) {
+static zs_status step_table_init_body(const zs_adam_hparams* hp, int32_t p, int32_t nsteps,
+                                      void* dev, size_t bytes, void* stream,
+                                      zs_step_table* table) {
   if (!table || !dev) return ZS_ERR_NULL;
   if (const zs_status st = check_hparams(hp)) return st;
-  if (p < 1 || p > ZS_MAX_P || nsteps < 1) return ZS_ERR_ARG;
+  if (p < 1 || p > ZS_MAX_P || nsteps < 1 || nsteps > ZS_MAX_TABLE_STEPS) return ZS_ERR_ARG;
   if (hp->step > INT64_MAX - nsteps) return ZS_ERR_RANGE;
   const size_t need = zs_step_table_bytes(nsteps);
   if (reinterpret_cast<uintptr_t>(dev) % 256u != 0 || bytes < need) return ZS_ERR_CAPACITY;
@@ -703,6 +730,12 @@ zs_status zs_step_table_init(const zs_adam_hparams* hp, int32_t p, int32_t nstep
   table->form = hp->form;
   table->reserved = 0;
   return ZS_OK;
+}
+
+zs_status zs_step_table_init(const zs_adam_hparams* hp, int32_t p, int32_t nsteps, void* dev,
+                             size_t bytes, void* stream, zs_step_table* table) {
+  return zs::guard(
+      [&] { return step_table_init_body(hp, p, nsteps, dev, bytes, stream, table); });
 }
 
 zs_status zs_step_table_advance(const zs_step_table* table, void* stream) {

@@ -202,9 +202,11 @@ bool overlap(const Span& a, const Span& b) { return a.lo < b.hi && b.lo < a.hi; 
 
 }  // namespace
 
-extern "C" zs_status zs_cpu_adam_step(const void* g, int32_t grad_dtype, float* w, float* m,
-                                      float* v, void* param, int32_t param_dtype, int64_t len,
-                                      const zs_adam_hparams* hp, int32_t threads) {
+namespace {
+
+zs_status cpu_adam_body(const void* g, int32_t grad_dtype, float* w, float* m, float* v,
+                        void* param, int32_t param_dtype, int64_t len, const zs_adam_hparams* hp,
+                        int32_t threads) {
   if (!hp) return ZS_ERR_NULL;
   if (len < 0) return ZS_ERR_ARG;
   if (len > (int64_t{1} << 60)) return ZS_ERR_RANGE;
@@ -241,12 +243,36 @@ extern "C" zs_status zs_cpu_adam_step(const void* g, int32_t grad_dtype, float* 
   int64_t nt = threads > 0 ? threads : static_cast<int64_t>(std::thread::hardware_concurrency());
   nt = std::max<int64_t>(1, std::min<int64_t>(nt, (len + 65535) / 65536));
   const int64_t per = ((len + nt - 1) / nt + 15) / 16 * 16;
+  // Ranges 1.. go to new threads; if the system refuses a thread (or the
+  // pool's memory), the calling thread runs the ranges not handed out.  The
+  // result does not depend on which thread runs a range.
   std::vector<std::thread> pool;
-  for (int64_t t = 1; t < nt; ++t) {
-    const int64_t lo = std::min(len, t * per), hi = std::min(len, lo + per);
-    if (lo < hi) pool.emplace_back(fn, std::cref(job), lo, hi);
+  int64_t t_next = 1;
+  try {
+    pool.reserve(static_cast<size_t>(nt - 1));
+    for (; t_next < nt; ++t_next) {
+      const int64_t lo = std::min(len, t_next * per), hi = std::min(len, lo + per);
+      if (lo < hi) pool.emplace_back(fn, std::cref(job), lo, hi);
+    }
+  } catch (...) {
   }
   fn(job, 0, std::min(len, per));
+  for (int64_t t = t_next; t < nt; ++t) {
+    const int64_t lo = std::min(len, t * per), hi = std::min(len, lo + per);
+    if (lo < hi) fn(job, lo, hi);
+  }
   for (auto& th : pool) th.join();
   return ZS_OK;
+}
+
+}  // namespace
+
+extern "C" zs_status zs_cpu_adam_step(const void* g, int32_t grad_dtype, float* w, float* m,
+                                      float* v, void* param, int32_t param_dtype, int64_t len,
+                                      const zs_adam_hparams* hp, int32_t threads) {
+  try {
+    return cpu_adam_body(g, grad_dtype, w, m, v, param, param_dtype, len, hp, threads);
+  } catch (...) {
+    return ZS_ERR_RESOURCE;
+  }
 }

@@ -7,7 +7,22 @@
 
 #include <vector>
 
+#include "../../include/zshard.h"
+
 namespace zs {
+
+// Runs an entry point's body; a failure to obtain host memory or a thread
+// (std::bad_alloc, std::system_error) becomes ZS_ERR_RESOURCE instead of an
+// exception crossing the C interface.
+template <class F>
+zs_status guard(F&& f) noexcept {
+  try {
+    return f();
+  } catch (...) {
+    return ZS_ERR_RESOURCE;
+  }
+}
+
 
 enum : int { kF16 = 1, kBF16 = 2 };
 enum : int { kStandard = 0, kPage1Literal = 1, kSgd = 2, kSgdMomentum = 3 };

@@ -31,6 +31,7 @@
 #include <algorithm>
 #include <cmath>
 #include <condition_variable>
+#include <functional>
 #include <mutex>
 #include <thread>
 #include <vector>
@@ -68,8 +69,10 @@ constexpr int64_t kMaxBuckets = 4096;
 
 }  // namespace
 
-extern "C" zs_status zs_offload_step(const zs_offload_args* a, const zs_adam_hparams* hp,
-                                     int32_t mode, int32_t slot) {
+namespace {
+
+zs_status offload_body(const zs_offload_args* a, const zs_adam_hparams* hp, int32_t mode,
+                       int32_t slot) {
   if (!a || !hp) return ZS_ERR_NULL;
   if (mode < ZS_OFFLOAD_PLAIN || mode > ZS_OFFLOAD_DELAYED || slot < 0 || slot > 1)
     return ZS_ERR_ARG;
@@ -156,17 +159,85 @@ extern "C" zs_status zs_offload_step(const zs_offload_args* a, const zs_adam_hpa
 
   auto* g16d = static_cast<uint16_t*>(a->g16_dev);
   auto* g16h_recv = static_cast<uint16_t*>(a->g16_host[slot]);
-  // 1. the GPU's buckets and their copies to host memory, all queued at once
   std::vector<const uint16_t*> gb(static_cast<size_t>(a->p));
+  std::vector<uintptr_t> a16, a32;
+  a16.reserve(static_cast<size_t>(a->p) + 1);
+  a32.reserve(1);
+
+  // The host update's workers: thread t takes slice t of every bucket once
+  // the bucket's gradient is on the host.  They start before anything is
+  // enqueued, so a refused thread fails the call with nothing in flight.
+  const auto* g16h_use = static_cast<const uint16_t*>(
+      mode == ZS_OFFLOAD_DELAYED ? a->g16_host[1 - slot] : a->g16_host[slot]);
+  auto* ph = static_cast<uint16_t*>(a->param_host);
+  int64_t nt = a->threads > 0 ? a->threads
+                              : static_cast<int64_t>(std::thread::hardware_concurrency());
+  nt = std::max<int64_t>(1, std::min<int64_t>(nt, (bucket + 65535) / 65536));
+  std::mutex mu;
+  std::condition_variable cv_ready, cv_done;
+  int64_t ready = mode == ZS_OFFLOAD_DELAYED ? nb : 0;  // buckets whose gradient is here
+  std::vector<int64_t> done(static_cast<size_t>(nb), 0);  // workers finished per bucket
+  zs_status worker_status = ZS_OK;
+  auto stop = [&](zs_status st) {  // every waiting worker returns
+    std::lock_guard<std::mutex> lk(mu);
+    if (worker_status == ZS_OK) worker_status = st;
+    cv_ready.notify_all();
+  };
+  auto work = [&](int64_t t) {
+    for (int64_t b = 0; b < nb; ++b) {
+      {
+        std::unique_lock<std::mutex> lk(mu);
+        cv_ready.wait(lk, [&] { return ready > b || worker_status != ZS_OK; });
+        if (worker_status != ZS_OK) return;
+      }
+      const int64_t lo = b * bucket, hi = std::min(len, lo + bucket);
+      const int64_t per = ((hi - lo + nt - 1) / nt + 15) / 16 * 16;
+      const int64_t a0 = std::min(hi, lo + t * per), a1 = std::min(hi, a0 + per);
+      zs_status st = ZS_OK;
+      if (a0 < a1)
+        st = zs_cpu_adam_step(g16h_use + a0, a->grad_dtype, a->w + a0, um ? a->m + a0 : nullptr,
+                              uv ? a->v + a0 : nullptr, ph + a0, a->param_dtype, a1 - a0, hp, 1);
+      std::lock_guard<std::mutex> lk(mu);
+      if (st != ZS_OK && worker_status == ZS_OK) worker_status = st;
+      ++done[static_cast<size_t>(b)];
+      cv_done.notify_all();
+      if (worker_status != ZS_OK) {
+        cv_ready.notify_all();
+        return;
+      }
+    }
+  };
+  // Joins the workers on every way out of this call.
+  struct Pool {
+    std::vector<std::thread> th;
+    std::function<void()> on_exit;
+    ~Pool() {
+      if (on_exit) on_exit();
+      for (auto& x : th)
+        if (x.joinable()) x.join();
+    }
+  } pool;
+  if (update) {
+    try {
+      pool.th.reserve(static_cast<size_t>(nt));
+      for (int64_t t = 0; t < nt; ++t) pool.th.emplace_back(work, t);
+    } catch (...) {
+      stop(ZS_ERR_RESOURCE);
+      return ZS_ERR_RESOURCE;  // ~Pool joins the workers already started
+    }
+  }
+  // once the call ends, early or not, no worker waits for a bucket
+  pool.on_exit = [&] { stop(ZS_ERR_HIP); };
+
   for (int64_t b = 0; b < nb; ++b) {
     const int64_t lo = b * bucket, hi = std::min(len, lo + bucket);
-    std::vector<uintptr_t> a16;
+    a16.clear();
+    a32.clear();
     for (int32_t r = 0; r < a->p; ++r) {
       gb[r] = gp[r] + lo;
       a16.push_back(reinterpret_cast<uintptr_t>(gb[r]));
     }
     a16.push_back(reinterpret_cast<uintptr_t>(g16d + lo));
-    std::vector<uintptr_t> a32;
     if (a->p > ZS_KERNARG_P) a32.push_back(reinterpret_cast<uintptr_t>(a->partial + lo));
     err = zs::mean_range(gb.data(), a->p, a->grad_dtype, hi - lo, zs::choose_head(a16, a32),
                          g16d + lo, a->grad_dtype, a->partial ? a->partial + lo : nullptr, cs);
@@ -176,55 +247,13 @@ extern "C" zs_status zs_offload_step(const zs_offload_args* a, const zs_adam_hpa
       err = hipMemcpyAsync(g16h_recv + lo, g16d + lo, 2u * static_cast<size_t>(hi - lo),
                            hipMemcpyDeviceToHost, ds);
     if (err == hipSuccess) err = hipEventRecord(copied.ev[b], ds);
-    if (err != hipSuccess) return fail(err);
+    if (err != hipSuccess) {
+      stop(fail(err));
+      (void)hipStreamSynchronize(ds);
+      return fail(err);
+    }
   }
-  // 2. the host update, bucket by bucket, each bucket's parameters sent back
-  // as soon as they are ready.  One set of worker threads for the whole call
-  // (starting threads per bucket cost more than small buckets take): worker t
-  // updates its share of every bucket in turn, as soon as the bucket's
-  // gradient is in host memory; this thread waits for the copies, releases
-  // the buckets, and queues each bucket's parameter copy when every worker
-  // has finished it.
   if (update) {
-    const auto* g16h_use = static_cast<const uint16_t*>(
-        mode == ZS_OFFLOAD_DELAYED ? a->g16_host[1 - slot] : a->g16_host[slot]);
-    auto* ph = static_cast<uint16_t*>(a->param_host);
-    int64_t nt = a->threads > 0 ? a->threads
-                                : static_cast<int64_t>(std::thread::hardware_concurrency());
-    nt = std::max<int64_t>(1, std::min<int64_t>(nt, (bucket + 65535) / 65536));
-    std::mutex mu;
-    std::condition_variable cv_ready, cv_done;
-    int64_t ready = mode == ZS_OFFLOAD_DELAYED ? nb : 0;  // buckets whose gradient is here
-    std::vector<int64_t> done(static_cast<size_t>(nb), 0);  // workers finished per bucket
-    zs_status worker_status = ZS_OK;
-    auto work = [&](int64_t t) {
-      for (int64_t b = 0; b < nb; ++b) {
-        {
-          std::unique_lock<std::mutex> lk(mu);
-          cv_ready.wait(lk, [&] { return ready > b || worker_status != ZS_OK; });
-          if (worker_status != ZS_OK) return;
-        }
-        const int64_t lo = b * bucket, hi = std::min(len, lo + bucket);
-        // contiguous shares on 16-element (64-byte fp32 line) boundaries
-        const int64_t per = ((hi - lo + nt - 1) / nt + 15) / 16 * 16;
-        const int64_t a0 = std::min(hi, lo + t * per), a1 = std::min(hi, a0 + per);
-        zs_status st = ZS_OK;
-        if (a0 < a1)
-          st = zs_cpu_adam_step(g16h_use + a0, a->grad_dtype, a->w + a0,
-                                um ? a->m + a0 : nullptr, uv ? a->v + a0 : nullptr, ph + a0,
-                                a->param_dtype, a1 - a0, hp, 1);
-        std::lock_guard<std::mutex> lk(mu);
-        if (st != ZS_OK && worker_status == ZS_OK) worker_status = st;
-        ++done[static_cast<size_t>(b)];
-        cv_done.notify_all();
-        if (worker_status != ZS_OK) {
-          cv_ready.notify_all();
-          return;
-        }
-      }
-    };
-    std::vector<std::thread> pool;
-    for (int64_t t = 0; t < nt; ++t) pool.emplace_back(work, t);
     zs_status st = ZS_OK;
     for (int64_t b = 0; b < nb && st == ZS_OK; ++b) {
       const int64_t lo = b * bucket, hi = std::min(len, lo + bucket);
@@ -252,21 +281,25 @@ extern "C" zs_status zs_offload_step(const zs_offload_args* a, const zs_adam_hpa
                            hipMemcpyHostToDevice, hs);
       if (err != hipSuccess) {
         st = fail(err);
-        std::lock_guard<std::mutex> lk(mu);
-        worker_status = st;
-        cv_ready.notify_all();
+        stop(st);
       }
     }
-    for (auto& th : pool) th.join();
     if (st != ZS_OK) {
+      stop(st);
       (void)hipStreamSynchronize(ds);
       (void)hipStreamSynchronize(hs);
       return st;
     }
   }
-  // 3. everything this call started is complete before it returns
   err = hipStreamSynchronize(ds);
   if (err == hipSuccess) err = hipStreamSynchronize(hs);
   if (err != hipSuccess) return fail(err);
   return ZS_OK;
+}
+
+}  // namespace
+
+extern "C" zs_status zs_offload_step(const zs_offload_args* a, const zs_adam_hparams* hp,
+                                     int32_t mode, int32_t slot) {
+  return zs::guard([&] { return offload_body(a, hp, mode, slot); });
 }

@@ -15,13 +15,14 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libzshard.so")
 
 ZS_OK, ZS_ERR_NULL, ZS_ERR_ARG, ZS_ERR_DTYPE, ZS_ERR_RANGE, ZS_ERR_ALIAS, ZS_ERR_CAPACITY, \
-    ZS_ERR_HIP, ZS_ERR_UNSUPPORTED = range(9)
+    ZS_ERR_HIP, ZS_ERR_UNSUPPORTED, ZS_ERR_RESOURCE = range(10)
 ZS_F16, ZS_BF16 = 1, 2
 ZS_ADAM_STANDARD, ZS_ADAM_PAGE1_LITERAL, ZS_SGD, ZS_SGD_MOMENTUM = 0, 1, 2, 3
 ZS_STATE_M, ZS_STATE_V = 1, 2
 ZS_MAX_P = 1024
 ZS_KERNARG_P = 256
 ZS_STATIC_SCRATCH_BYTES = 8192
+ZS_MAX_TABLE_STEPS = 1 << 24
 
 FORMS = {"standard": ZS_ADAM_STANDARD, "page1_literal": ZS_ADAM_PAGE1_LITERAL, "sgd": ZS_SGD,
          "sgd_momentum": ZS_SGD_MOMENTUM}

@@ -30,6 +30,8 @@
  *    launched, and leave every buffer untouched.  A failed launch returns
  *    ZS_ERR_HIP (zs_last_hip_error() gives the hipError_t).  A fault inside a
  *    kernel surfaces at the caller's next synchronisation, as in any HIP code.
+ *    Host memory the call needs for its own bookkeeping that cannot be had
+ *    gives ZS_ERR_RESOURCE (no exception crosses this interface).
  *  - Shards that are empty (s_k == e_k) return ZS_OK without launching.
  *  - No alignment is required.  Arrays whose addresses line up on 16 bytes
  *    at a common element take the widest loads.
@@ -66,7 +68,8 @@ typedef enum {
   ZS_ERR_ALIAS = 5,    /* an output range overlaps another input or output range */
   ZS_ERR_CAPACITY = 6, /* a caller-provided table or workspace is too small */
   ZS_ERR_HIP = 7,      /* a HIP call failed; see zs_last_hip_error() */
-  ZS_ERR_UNSUPPORTED = 8 /* the host CPU lacks an instruction set the call needs */
+  ZS_ERR_UNSUPPORTED = 8, /* the host CPU lacks an instruction set the call needs */
+  ZS_ERR_RESOURCE = 9     /* host memory or a host thread could not be obtained */
 } zs_status;
 
 typedef enum { ZS_F16 = 1, ZS_BF16 = 2 } zs_dtype;
@@ -351,7 +354,12 @@ typedef struct {
   int32_t reserved;
 } zs_step_table;
 
-/* Device bytes of a step table of nsteps entries (0 if nsteps < 1). */
+/* Entries of one step table at most (36 bytes each on the device, staged
+ * once in host memory by zs_step_table_init). */
+#define ZS_MAX_TABLE_STEPS (1 << 24)
+
+/* Device bytes of a step table of nsteps entries (0 if nsteps is outside
+ * 1..ZS_MAX_TABLE_STEPS). */
 size_t zs_step_table_bytes(int32_t nsteps);
 
 /* Fills a step table for steps hp->step .. hp->step + nsteps - 1 with hp's
@@ -359,7 +367,8 @@ size_t zs_step_table_bytes(int32_t nsteps);
  * zs_step_table_bytes(nsteps) bytes, 256-byte aligned), with one
  * host-to-device copy on `stream`, and waits for it (not capturable; call it
  * before capture).  Errors: ZS_ERR_NULL, ZS_ERR_ARG (hparams, p outside
- * 1..ZS_MAX_P, nsteps < 1), ZS_ERR_CAPACITY, ZS_ERR_HIP. */
+ * 1..ZS_MAX_P, nsteps outside 1..ZS_MAX_TABLE_STEPS), ZS_ERR_CAPACITY,
+ * ZS_ERR_HIP, ZS_ERR_RESOURCE. */
 zs_status zs_step_table_init(const zs_adam_hparams* hp, int32_t p, int32_t nsteps, void* dev,
                              size_t bytes, void* stream, zs_step_table* table);
 

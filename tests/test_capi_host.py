@@ -40,8 +40,10 @@ def test_every_declared_symbol_is_exported():
         assert hasattr(L, n), n
     assert sorted(z.EXPORTS) == names
     assert z.zs_version() == 2
-    for st in range(8):
+    for st in range(10):
         assert z.zs_status_string(st).startswith("ZS_")
+        assert z.zs_status_string(st) != "ZS_ERR_UNKNOWN"
+    assert z.zs_status_string(z.ZS_ERR_RESOURCE) == "ZS_ERR_RESOURCE"
     assert z.zs_status_string(99) == "ZS_ERR_UNKNOWN"
 
 
@@ -386,11 +388,17 @@ def test_step_table_layout_and_errors():
     assert z.zs_step_table_bytes(1) == 256
     assert z.zs_step_table_bytes(5) == 256                 # 48 + 5 * 36 bytes
     assert z.zs_step_table_bytes(6) == 512
+    big = z.ZS_MAX_TABLE_STEPS
+    assert z.zs_step_table_bytes(big) == (48 + 36 * big + 255) // 256 * 256
+    assert z.zs_step_table_bytes(big + 1) == 0
     L = z.lib()
     import ctypes as C
 
     t = z.zs_step_table()
     assert L.zs_step_table_init(C.byref(HP), 8, 0, FAKE, 256, None, C.byref(t)) == z.ZS_ERR_ARG
+    # more entries than one table holds: refused before any host staging
+    assert L.zs_step_table_init(C.byref(HP), 8, big + 1, FAKE, 1 << 40, None, C.byref(t)) == \
+        z.ZS_ERR_ARG
     assert L.zs_step_table_init(C.byref(HP), 0, 4, FAKE, 256, None, C.byref(t)) == z.ZS_ERR_ARG
     assert L.zs_step_table_init(C.byref(HP), 1025, 4, FAKE, 256, None, C.byref(t)) == \
         z.ZS_ERR_ARG
@@ -406,6 +414,8 @@ def test_step_table_layout_and_errors():
     assert z.zs_step_table_advance(st, check=False) == z.ZS_ERR_NULL
     st.dev = FAKE
     st.nsteps = 0
+    assert z.zs_step_table_advance(st, check=False) == z.ZS_ERR_ARG
+    st.nsteps = big + 1
     assert z.zs_step_table_advance(st, check=False) == z.ZS_ERR_ARG
     st.nsteps, st.form = 4, 7
     assert z.zs_step_table_advance(st, check=False) == z.ZS_ERR_ARG
