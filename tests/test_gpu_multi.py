@@ -188,3 +188,16 @@ def test_two_hundred_ranks_with_whole_chunks():
     assert [pc[3] for pc in case.pieces] == [100_000, 7, 199_993]
     say(f"200 ranks: shard {k}, pieces {[pc[3] for pc in case.pieces]}, {case.nchunks} chunks")
     _run_and_check(case, 2, 49)
+
+
+@pytest.mark.parametrize("k,npieces", [(1, 1), (3, 25), (4, 27), (5, 25), (6, 26)])
+def test_gpt2_small_shapes_remaining_shards(k, npieces):
+    # the other ranks of the 8-way GPT-2 sharding, at the chunk length bench.py
+    # uses (short entries for the many-piece shards)
+    wl = WORKLOADS["gpt2_small_p8"]
+    numel = [n for _, n in wl.tensors]
+    chunk = _bench_chunk(numel, wl.p, k)
+    case = MtCase(numel, wl.p, k, wl.grad_dtype, wl.param_dtype, chunk, 60 + k)
+    assert len(case.pieces) == npieces
+    say(f"gpt2 shard {k}: {npieces} pieces, chunk {chunk}, 2 steps")
+    _run_and_check(case, 2, 70 + k)
