@@ -140,6 +140,69 @@ void phased_kernel(const char* __restrict__ src, char* __restrict__ dst, int64_t
   }
 }
 
+// The step's own read pattern and nothing else: P 16-bit rank buffers read
+// in whole chunks of 28 groups of 2048 elements, round-robin over the
+// workgroups; per chunk, rank by rank, each lane's first 16-byte load alone
+// (its address translation taken with one load waiting), then the chunk's 27
+// other loads back to back, every load widened (fp16) and added into fp32
+// sums per element in rank order, as the fused step's read phase does.
+constexpr int kStepGroups = 28;
+constexpr int kStepRanks = 64;
+struct StepRanks {
+  const uint16_t* g[kStepRanks];
+};
+
+__device__ __forceinline__ float h_lo(uint32_t x) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(x & 0xffffu)));
+}
+__device__ __forceinline__ float h_hi(uint32_t x) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(x >> 16)));
+}
+__device__ __forceinline__ void add8(float (&a)[8], const u32x4& q) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    a[2 * j] += h_lo(q[j]);
+    a[2 * j + 1] += h_hi(q[j]);
+  }
+}
+
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void step_reads_kernel(StepRanks R, int p, int64_t nchunks, u32x4* __restrict__ sink) {
+  const uint32_t off = threadIdx.x * 16u;
+  constexpr int64_t kChunk = static_cast<int64_t>(kStepGroups) * kBlock * 8;  // elements
+  float keep = 0.0f;
+  for (int64_t ch = blockIdx.x; ch < nchunks; ch += gridDim.x) {
+    float s[kStepGroups][8];
+#pragma unroll
+    for (int u = 0; u < kStepGroups; ++u)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s[u][j] = 0.0f;
+    for (int r = 0; r < p; ++r) {
+      const char* base = reinterpret_cast<const char*>(R.g[r] + ch * kChunk) + off;
+      {
+        const u32x4 q0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base));
+        __builtin_amdgcn_sched_barrier(0);
+        add8(s[0], q0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      u32x4 q[kStepGroups - 1];
+#pragma unroll
+      for (int u = 0; u < kStepGroups - 1; ++u)
+        q[u] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(base + static_cast<int64_t>(1 + u) * kBlock * 16));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < kStepGroups - 1; ++u) add8(s[1 + u], q[u]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int u = 0; u < kStepGroups; ++u)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) keep += s[u][j];
+  }
+  if (keep == 123456.0f) sink[threadIdx.x] = u32x4{1u, 2u, 3u, 4u};  // keeps the sums
+}
+
 template <int NR, int NW, int G>
 hipError_t run_phased(const void* src, void* dst, int64_t stream_bytes, int64_t nvec, int grid,
                       void* sink, hipStream_t s) {
@@ -187,6 +250,20 @@ int32_t zsp_stream(int32_t mix, const void* src, void* dst, int64_t stream_bytes
     default: return 1;
   }
   return e == hipSuccess ? 0 : 2;
+}
+
+int32_t zsp_step_reads(const void* const* ranks, int32_t p, int64_t elems, int32_t grid,
+                       void* sink, void* stream) {
+  if (!ranks || !sink || p < 1 || p > kStepRanks || elems < 0 || grid < 1) return 1;
+  StepRanks R;
+  for (int r = 0; r < kStepRanks; ++r) {
+    R.g[r] = r < p ? static_cast<const uint16_t*>(ranks[r]) : nullptr;
+    if (r < p && !R.g[r]) return 1;
+  }
+  const int64_t nchunks = elems / (static_cast<int64_t>(kStepGroups) * kBlock * 8);
+  step_reads_kernel<<<dim3(grid), dim3(kBlock), 0, static_cast<hipStream_t>(stream)>>>(
+      R, p, nchunks, static_cast<u32x4*>(sink));
+  return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
 int32_t zsp_streams(int32_t mix, int32_t* nread, int32_t* nwrite) {

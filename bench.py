@@ -663,6 +663,46 @@ def ceiling(args):
               file=sys.stderr, flush=True)
         del src, dst
         torch.cuda.empty_cache()
+    # the fused step's read phase alone, in its own pattern: the 64 rank
+    # slices of the 7.5B-parameter shard (fp16), whole chunks only
+    P.zsp_step_reads.argtypes = [C.POINTER(C.c_void_p), C.c_int32, C.c_int64, C.c_int32,
+                                 C.c_void_p, C.c_void_p]
+    P.zsp_step_reads.restype = C.c_int32
+    from adam_zs_shard_amd import zshard as z
+    from zs_synth import WORKLOADS
+
+    wl = WORKLOADS["zero_7p5b_p64"]
+    M, _, _ = z.zs_plan_shards(wl.n, wl.p)
+    ranks = [torch.empty(M, dtype=torch.float16, device="cuda").normal_(0.0, 1e-3)
+             for _ in range(wl.p)]
+    arr = (C.c_void_p * wl.p)(*[g.data_ptr() for g in ranks])
+    chunk = 28 * 256 * 8
+    moved = (M // chunk) * chunk * 2 * wl.p
+
+    def launch_reads():
+        rc = P.zsp_step_reads(arr, wl.p, M, ncu, sink.data_ptr(), stream.cuda_stream)
+        assert rc == 0, f"probe step_reads failed ({rc})"
+
+    for _ in range(2):
+        launch_reads()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        launch_reads()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    gbs = moved / (ms / 1e3) / 1e9
+    out["step_reads_p64"] = {"streams_read": wl.p, "streams_written": 0, "bytes_per_launch": moved,
+                             "best_gbs": round(gbs, 1), "best_frac_of_8tbs": round(gbs / HBM_PEAK_GBS, 4),
+                             "best_workgroups_per_cu": 1, "best_ms": round(ms, 4),
+                             "gbs_by_workgroups_per_cu": {"1_per_cu": round(gbs, 1)},
+                             "step_bytes_per_element": None}
+    print(f"[ceiling] step_reads_p64: {gbs:.0f} GB/s ({ms:.3f} ms)", file=sys.stderr, flush=True)
+    del ranks
+    torch.cuda.empty_cache()
     print(json.dumps({"ceiling": out, "peak_gbs": HBM_PEAK_GBS, "cus": ncu}), flush=True)
 
 

@@ -48,6 +48,18 @@ int32_t zsp_streams(int32_t mix, int32_t* nread, int32_t* nwrite);
 int32_t zsp_stream(int32_t mix, const void* src, void* dst, int64_t stream_bytes, int64_t nvec,
                    int32_t grid, void* sink, void* stream);
 
+/* The fused step's read phase alone, in its own pattern: p <= 64 rank
+ * buffers of 16-bit values (fp16), each at least `elems` elements; the
+ * whole chunks of 57,344 elements (elems / 57,344 of them) go round-robin
+ * over `grid` workgroups of 256 lanes; per chunk, rank by rank, a first
+ * load per lane alone, then the other 27 back to back, summed in fp32 in
+ * rank order ([DP-III] §(四) step 2).  Reads 2 * p * 57,344 bytes per
+ * chunk and writes nothing but, never in practice, `sink` (4 KiB of device
+ * memory).  Returns 0, 1 on bad arguments (nothing launched), 2 if the
+ * launch failed. */
+int32_t zsp_step_reads(const void* const* ranks, int32_t p, int64_t elems, int32_t grid,
+                       void* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,7 +30,7 @@ def probe():
 def test_exports_every_declared_function(probe):
     text = open(os.path.join(ROOT, "include", "zsprobe.h")).read()
     names = re.findall(r"^int32_t (\w+)\(", text, re.M)
-    assert sorted(names) == ["zsp_stream", "zsp_streams"]
+    assert sorted(names) == ["zsp_step_reads", "zsp_stream", "zsp_streams"]
     for n in names:
         assert hasattr(probe, n), n
 
@@ -65,3 +65,15 @@ def test_bad_arguments_launch_nothing(probe):
     assert probe.zsp_stream(0, fake, None, 1000, 1024, 256, fake, None) == 1         # streams overlap
     assert probe.zsp_stream(1, fake, None, 1 << 20, 1024, 256, fake, None) == 1      # copy, no dst
     assert probe.zsp_stream(99, fake, fake, 1 << 20, 1024, 256, fake, None) == 1     # unknown mix
+    probe.zsp_step_reads.argtypes = [C.POINTER(C.c_void_p), C.c_int32, C.c_int64, C.c_int32,
+                                     C.c_void_p, C.c_void_p]
+    probe.zsp_step_reads.restype = C.c_int32
+    ranks = (C.c_void_p * 65)(*([fake] * 65))
+    assert probe.zsp_step_reads(None, 8, 1 << 20, 256, fake, None) == 1             # no ranks
+    assert probe.zsp_step_reads(ranks, 65, 1 << 20, 256, fake, None) == 1           # p > 64
+    assert probe.zsp_step_reads(ranks, 0, 1 << 20, 256, fake, None) == 1            # p < 1
+    assert probe.zsp_step_reads(ranks, 8, 1 << 20, 0, fake, None) == 1              # grid 0
+    assert probe.zsp_step_reads(ranks, 8, -1, 256, fake, None) == 1                 # elems < 0
+    assert probe.zsp_step_reads(ranks, 8, 1 << 20, 256, None, None) == 1            # no sink
+    holes = (C.c_void_p * 8)(*([fake] * 7 + [None]))
+    assert probe.zsp_step_reads(holes, 8, 1 << 20, 256, fake, None) == 1            # a null rank
