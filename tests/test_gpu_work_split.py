@@ -5,8 +5,8 @@ The kernel runs whole chunks (28 vectors of 8 elements per lane, 57,344
 elements per block) in balanced rounds over its blocks (one per CU), keeps a
 last partial round only when it fills at least half of the blocks, and
 deals the rest out as two-vector pieces.  A shard under half a whole chunk
-per CU goes to the small-shard kernel instead (pieces only, four workgroups
-per CU).  The shard lengths below are chosen
+per CU goes to the small-shard kernel instead (pieces only, three
+workgroups per CU).  The shard lengths below are chosen
 from the device's CU count to land in each regime: a last round under half
 full (whole rounds + pieces), one over half full (whole chunks only, plus a
 short tail), a shard smaller than one round (pieces only), and lengths that
