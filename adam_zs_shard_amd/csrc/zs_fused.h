@@ -111,12 +111,24 @@ void fused_kernel(GradArgs<PMAX> ga, int p, float* __restrict__ w, float* __rest
       float W[kVec] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
       float M[kVec] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
       float V[kVec] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      // state stores as whole lines (1 KiB per wave instruction); with Adam
+      // the moments' stores go out before the weight arithmetic
+      if constexpr (FORM == kStandard || FORM == kPage1Literal) {
+        float g[kVec], MH[kVec], VH[kVec];
 #pragma unroll
-      for (int j = 0; j < kVec; ++j) adam1<FORM>(c, s[u][j] / c.PF, W[j], M[j], V[j]);
-      // state stores as whole lines (1 KiB per wave instruction)
-      st_f32x8_lines(wb, so, W);
-      if constexpr (kUsesM<FORM>) st_f32x8_lines(mb, so, M);
-      if constexpr (kUsesV<FORM>) st_f32x8_lines(vb, so, V);
+        for (int j = 0; j < kVec; ++j) g[j] = s[u][j] / c.PF;
+        adam_moments8<FORM>(c, g, M, V, MH, VH);
+        st_f32x8_lines(mb, so, M);
+        st_f32x8_lines(vb, so, V);
+        __builtin_amdgcn_sched_barrier(0);
+        adam_weights8(c, MH, VH, W);
+        st_f32x8_lines(wb, so, W);
+      } else {
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) adam1<FORM>(c, s[u][j] / c.PF, W[j], M[j], V[j]);
+        st_f32x8_lines(wb, so, W);
+        if constexpr (kUsesM<FORM>) st_f32x8_lines(mb, so, M);
+      }
       st_u16x8(par + e0, lane16,
                u32x4{narrow2<PDT>(W[0], W[1]), narrow2<PDT>(W[2], W[3]),
                      narrow2<PDT>(W[4], W[5]), narrow2<PDT>(W[6], W[7])});
