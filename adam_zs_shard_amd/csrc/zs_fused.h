@@ -98,22 +98,26 @@ void fused_kernel(GradArgs<PMAX> ga, int p, float* __restrict__ w, float* __rest
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // update phase: mean, Adam, stores, group by group
+    // update phase: mean, Adam, stores, group by group; state stores as whole
+    // lines (1 KiB per wave instruction)
+    if constexpr (FORM == kStandard || FORM == kPage1Literal) {
+      // Each group's Adam in two halves: the m and v stores go out after the
+      // moments, then the next group's state loads, then the weight
+      // arithmetic and the w and working-copy stores, so the stores leave in
+      // two bursts and the next loads are in flight during the divisions.
+      const int64_t eb = h + g0 * kVec;
+      f32x4 nw0 = ld_f32x4(w + eb, lane32), nw1 = ld_f32x4(w + eb, lane32 + 16);
+      f32x4 nm0 = ld_f32x4(m + eb, lane32), nm1 = ld_f32x4(m + eb, lane32 + 16);
+      f32x4 nv0 = ld_f32x4(v + eb, lane32), nv1 = ld_f32x4(v + eb, lane32 + 16);
 #pragma unroll
-    for (int u = 0; u < kGroupsMax; ++u) {
-      const int64_t e0 = h + (g0 + static_cast<int64_t>(u) * kBlock) * kVec;
-      float* wb = w + e0;
-      float* mb = m + e0;
-      float* vb = v + e0;
-      const f32x4 w0 = ld_f32x4(wb, lane32), w1 = ld_f32x4(wb, lane32 + 16);
-      const f32x4 m0 = ld_state<kUsesM<FORM>>(mb, lane32), m1 = ld_state<kUsesM<FORM>>(mb, lane32 + 16);
-      const f32x4 v0 = ld_state<kUsesV<FORM>>(vb, lane32), v1 = ld_state<kUsesV<FORM>>(vb, lane32 + 16);
-      float W[kVec] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-      float M[kVec] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-      float V[kVec] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-      // state stores as whole lines (1 KiB per wave instruction); with Adam
-      // the moments' stores go out before the weight arithmetic
-      if constexpr (FORM == kStandard || FORM == kPage1Literal) {
+      for (int u = 0; u < kGroupsMax; ++u) {
+        const int64_t e0 = h + (g0 + static_cast<int64_t>(u) * kBlock) * kVec;
+        float* wb = w + e0;
+        float* mb = m + e0;
+        float* vb = v + e0;
+        float W[kVec] = {nw0.x, nw0.y, nw0.z, nw0.w, nw1.x, nw1.y, nw1.z, nw1.w};
+        float M[kVec] = {nm0.x, nm0.y, nm0.z, nm0.w, nm1.x, nm1.y, nm1.z, nm1.w};
+        float V[kVec] = {nv0.x, nv0.y, nv0.z, nv0.w, nv1.x, nv1.y, nv1.z, nv1.w};
         float g[kVec], MH[kVec], VH[kVec];
 #pragma unroll
         for (int j = 0; j < kVec; ++j) g[j] = s[u][j] / c.PF;
@@ -121,17 +125,42 @@ void fused_kernel(GradArgs<PMAX> ga, int p, float* __restrict__ w, float* __rest
         st_f32x8_lines(mb, so, M);
         st_f32x8_lines(vb, so, V);
         __builtin_amdgcn_sched_barrier(0);
+        if (u + 1 < kGroupsMax) {
+          nw0 = ld_f32x4(wb + kGroup, lane32);
+          nw1 = ld_f32x4(wb + kGroup, lane32 + 16);
+          nm0 = ld_f32x4(mb + kGroup, lane32);
+          nm1 = ld_f32x4(mb + kGroup, lane32 + 16);
+          nv0 = ld_f32x4(vb + kGroup, lane32);
+          nv1 = ld_f32x4(vb + kGroup, lane32 + 16);
+        }
+        __builtin_amdgcn_sched_barrier(0);
         adam_weights8(c, MH, VH, W);
         st_f32x8_lines(wb, so, W);
-      } else {
+        st_u16x8(par + e0, lane16,
+                 u32x4{narrow2<PDT>(W[0], W[1]), narrow2<PDT>(W[2], W[3]),
+                       narrow2<PDT>(W[4], W[5]), narrow2<PDT>(W[6], W[7])});
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kGroupsMax; ++u) {
+        const int64_t e0 = h + (g0 + static_cast<int64_t>(u) * kBlock) * kVec;
+        float* wb = w + e0;
+        float* mb = m + e0;
+        const f32x4 w0 = ld_f32x4(wb, lane32), w1 = ld_f32x4(wb, lane32 + 16);
+        const f32x4 m0 = ld_state<kUsesM<FORM>>(mb, lane32);
+        const f32x4 m1 = ld_state<kUsesM<FORM>>(mb, lane32 + 16);
+        float W[kVec] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        float M[kVec] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+        float V[kVec] = {};  // unused by the SGD forms
 #pragma unroll
         for (int j = 0; j < kVec; ++j) adam1<FORM>(c, s[u][j] / c.PF, W[j], M[j], V[j]);
         st_f32x8_lines(wb, so, W);
         if constexpr (kUsesM<FORM>) st_f32x8_lines(mb, so, M);
+        st_u16x8(par + e0, lane16,
+                 u32x4{narrow2<PDT>(W[0], W[1]), narrow2<PDT>(W[2], W[3]),
+                       narrow2<PDT>(W[4], W[5]), narrow2<PDT>(W[6], W[7])});
       }
-      st_u16x8(par + e0, lane16,
-               u32x4{narrow2<PDT>(W[0], W[1]), narrow2<PDT>(W[2], W[3]),
-                     narrow2<PDT>(W[4], W[5]), narrow2<PDT>(W[6], W[7])});
     }
   }
   fused_rest<GDT, PDT, FORM>(gr, p, w, m, v, par, len, h, nvec, nfull * kFull, nfull, c,
