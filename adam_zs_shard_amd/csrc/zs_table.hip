@@ -97,12 +97,24 @@ void table_kernel(TableSrc src, int p, Consts c0, const StepTableDev* st) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      // update phase: mean, Adam, stores, group by group
+      // update phase: mean, Adam, stores, group by group (Adam: the next
+      // group's state loads between each group's moment and weight halves)
+      if constexpr (FORM == kStandard || FORM == kPage1Literal) {
+        GroupState q = load_group<FORM>(L, w, m, v, h + g0 * kVec);
 #pragma unroll
-      for (int u = 0; u < kGroupsMax; ++u) {
-        const int64_t e0 = h + (g0 + static_cast<int64_t>(u) * kBlock) * kVec;
-        const GroupState q = load_group<FORM>(L, w, m, v, e0);
-        apply_group<PDT, FORM>(c, L, q, s[u], w, m, v, par, e0);
+        for (int u = 0; u < kGroupsMax; ++u) {
+          const int64_t e0 = h + (g0 + static_cast<int64_t>(u) * kBlock) * kVec;
+          GroupState qn = q;
+          apply_group_pipe<PDT, FORM>(c, L, q, s[u], w, m, v, par, e0, u + 1 < kGroupsMax, qn);
+          q = qn;
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < kGroupsMax; ++u) {
+          const int64_t e0 = h + (g0 + static_cast<int64_t>(u) * kBlock) * kVec;
+          const GroupState q = load_group<FORM>(L, w, m, v, e0);
+          apply_group<PDT, FORM>(c, L, q, s[u], w, m, v, par, e0);
+        }
       }
     }
     // the rest in rank batches of 8 (1% faster than 16 on the 35-piece GPT-2
