@@ -226,7 +226,8 @@ zs_status offload_body(const zs_offload_args* a, const zs_adam_hparams* hp, int3
       return ZS_ERR_RESOURCE;  // ~Pool joins the workers already started
     }
   }
-  // once the call ends, early or not, no worker waits for a bucket
+  // once the call ends, early or not, no worker waits for a bucket: any
+  // non-OK status wakes the ones still waiting (after a normal end, none is)
   pool.on_exit = [&] { stop(ZS_ERR_HIP); };
 
   for (int64_t b = 0; b < nb; ++b) {
