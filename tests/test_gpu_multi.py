@@ -201,3 +201,51 @@ def test_gpt2_small_shapes_remaining_shards(k, npieces):
     assert len(case.pieces) == npieces
     say(f"gpt2 shard {k}: {npieces} pieces, chunk {chunk}, 2 steps")
     _run_and_check(case, 2, 70 + k)
+
+
+def test_grid_barrier_launch_equals_plain_launch():
+    # A table of 24 rounds of whole chunks (one 57,344-element entry per CU
+    # and round) takes the cooperative launch with grid-wide barriers when the
+    # constants come by value; through a step table it takes the plain
+    # launch.  Same inputs, same state: the two must agree bit for bit, and
+    # sampled elements must match the oracle.
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    chunk = 28 * 256 * 8
+    p = 2
+    L = 24 * ncu * chunk + 12_345            # 24 full rounds and a ragged tail
+    numel = [L * p]
+    say(f"grid-barrier table: {L} elements per shard, {24 * ncu} whole chunks")
+    cases = [MtCase(numel, p, 1, "bf16", "bf16", chunk, 81) for _ in range(2)]
+    assert cases[0].nchunks >= 24 * ncu
+    for c in cases:
+        c.set_grads(1, 82)
+    hp = z.hparams(LR, B1, B2, EPS, 1)
+    z.zs_fused_shard_step_multi(cases[0].table, hp)                     # cooperative
+    nb = z.zs_step_table_bytes(1)
+    stdev = torch.empty(nb, dtype=torch.uint8, device=DEV)
+    steps = z.zs_step_table_init(hp, p, 1, stdev, nb)
+    z.zs_fused_shard_step_multi_dev(cases[1].table, steps)              # plain
+    torch.cuda.synchronize()
+    for name in ("w", "m", "v"):
+        a, b = getattr(cases[0], name), getattr(cases[1], name)
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), name
+    pa, pb = cases[0].params[0], cases[1].params[0]
+    assert torch.equal(pa.view(torch.int16), pb.view(torch.int16))
+    # oracle on sampled elements of the shard (every CU's first and last chunk
+    # of the first and last rounds, and the tail)
+    c0 = cases[0]
+    idx = np.unique(np.concatenate([
+        np.arange(0, 64), np.arange(chunk - 64, chunk + 64),
+        np.arange((ncu - 1) * chunk, ncu * chunk, 997),
+        np.arange(23 * ncu * chunk, 23 * ncu * chunk + 4096, 13),
+        np.arange(L - 12_345, L)]))
+    gb = [g[idx] for g in c0.gbits]
+    wh = c0.w0.numpy()[idx].copy()
+    mh = np.zeros_like(wh)
+    vh = np.zeros_like(wh)
+    ph = oracle_step_threaded("bf16", gb, wh, mh, vh, "bf16", 1, "standard")
+    d = check_f32(f32(c0.w)[idx], wh, 1e-6, "w")
+    d += check_f32(f32(c0.m)[idx], mh, 1e-6, "m")
+    d += check_f32(f32(c0.v)[idx], vh, 1e-6, "v")
+    d += check_param(u16(pa)[c0.s + idx], ph, "bf16", "param")
+    assert d == 0
