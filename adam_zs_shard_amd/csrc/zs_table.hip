@@ -7,12 +7,6 @@
 namespace zs {
 namespace {
 
-// Multi-tensor fused step, one workgroup per CU, one wave per SIMD: for each
-// chunk-table entry, the whole chunks of the entry, then its rest, by the
-// block that took the entry.  Entries go round-robin in rounds of gridDim.x;
-// SYNC > 0 adds a grid-wide barrier every SYNC rounds (every block takes the
-// same number of barriers, with or without an entry in the round).  The body is the single-tensor kernel's (see
-// fused_kernel below for why it is written out rather than factored).
 // Rounds of entries between two grid-wide barriers (SYNC > 0, cooperative
 // launches only).  With one workgroup per CU the CUs drift out of step over
 // the rounds, until about a third of them read gradients while the rest
@@ -22,6 +16,13 @@ namespace {
 // slower than none).
 constexpr int kTableSyncRounds = 12;
 
+// Multi-tensor fused step, one workgroup per CU, one wave per SIMD: for each
+// chunk-table entry, the whole chunks of the entry, then its rest, by the
+// block that took the entry.  Entries go round-robin in rounds of gridDim.x;
+// SYNC > 0 adds a grid-wide barrier every SYNC rounds (every block takes the
+// same number of barriers, with or without an entry in the round).  The body
+// is the single-tensor kernel's (see fused_kernel for why it is written out
+// rather than factored).
 template <int GDT, int PDT, int FORM, int SYNC = 0>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void table_kernel(TableSrc src, int p, Consts c0, const StepTableDev* st) {
@@ -138,11 +139,10 @@ void table_kernel(TableSrc src, int p, Consts c0, const StepTableDev* st) {
     }
     // the rest in rank batches of 8 (1% faster than 16 on the 35-piece GPT-2
     // shard; with fp16 gradients, 16 spilled)
-    fused_rest<GDT, PDT, FORM, 8>(gr, p, w, m, v, par, R.len, h, nvec,
-                                                     nfull * kFull, nfull, c, R.blk, R.nblk, L);
+    fused_rest<GDT, PDT, FORM, 8>(gr, p, w, m, v, par, R.len, h, nvec, nfull * kFull, nfull, c,
+                                  R.blk, R.nblk, L);
   }
 }
-
 
 // Tables whose entries are all shorter than a whole chunk (so table_kernel
 // would run only its rest path): the same pieces of two groups, over two
