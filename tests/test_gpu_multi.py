@@ -249,3 +249,38 @@ def test_grid_barrier_launch_equals_plain_launch():
     d += check_f32(f32(c0.v)[idx], vh, 1e-6, "v")
     d += check_param(u16(pa)[c0.s + idx], ph, "bf16", "param")
     assert d == 0
+
+
+def test_long_table_captured_by_value_takes_plain_launch():
+    # The same 24-round table with its constants by value, launched on a
+    # stream under capture: the launcher must not try the cooperative launch
+    # there.  Two replays of the graph must equal two eager (cooperative)
+    # launches of the same step on a copy with the same state.
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    chunk = 28 * 256 * 8
+    p = 2
+    L = 24 * ncu * chunk + 777
+    numel = [L * p]
+    say(f"captured long table: {L} elements per shard")
+    eager, graphed = (MtCase(numel, p, 1, "bf16", "bf16", chunk, 83) for _ in range(2))
+    for c in (eager, graphed):
+        c.set_grads(1, 84)
+    hp = z.hparams(LR, B1, B2, EPS, 1)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g):
+            z.zs_fused_shard_step_multi(graphed.table, hp,
+                                        stream=torch.cuda.current_stream().cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(graphed.w, graphed.w0.to(DEV))  # capture ran nothing
+    for rep in range(2):
+        z.zs_fused_shard_step_multi(eager.table, hp)
+        g.replay()
+        torch.cuda.synchronize()
+        for name in ("w", "m", "v"):
+            a, b = getattr(eager, name), getattr(graphed, name)
+            assert torch.equal(a.view(torch.int32), b.view(torch.int32)), (rep, name)
+        assert torch.equal(eager.params[0].view(torch.int16), graphed.params[0].view(torch.int16)), rep
