@@ -34,6 +34,9 @@
 //    ranks batched, so the workgroups finish together.  Shards under half a
 //    chunk per CU get no whole chunk: small_kernel deals their pieces over
 //    three workgroups per CU instead.
+//  - Soft barriers: with one workgroup per CU the CUs drift apart over the
+//    rounds of chunks until reads and writes mix again; every few rounds a
+//    soft barrier (soft_barrier below) pulls the grid back into step.
 //  - No MFMA and no LDS on the single-tensor path (nothing is reused); the
 //    multi-tensor path stages one chunk's descriptors in LDS.
 // Arithmetic (rank-order fp32 mean, Adam moments, bias correction, update,
@@ -78,6 +81,55 @@ constexpr int kLoadBatch = 28;
 constexpr int kTableLoadBatch = 14;
 static_assert(kGroupsMax % kLoadBatch == 0, "whole load batches per chunk");
 static_assert(kGroupsMax % kTableLoadBatch == 0, "whole load batches per chunk");
+
+// Soft barrier.  One workgroup per CU starts every round of chunks with its
+// read phase, but the CUs do not run at one speed (some XCDs run 1-2.5%
+// slower for a whole launch, and a round's time varies by 7-14% from CU to
+// CU), so after a few rounds some CUs read gradients while others update,
+// and HBM serves that mix more slowly than the two phases apart.  A grid-wide
+// barrier would put them back in step but waits for the slowest workgroup
+// every time.  This one waits only for most of the grid: thread 0 counts its
+// workgroup in, then waits until kSoftPct percent of the grid has arrived,
+// the last arrival has reset the count for the slot's next use, or
+// kSoftCapTicks of the 100 MHz real-time clock have passed.  It orders no
+// data (no workgroup reads what another writes), so results never depend on
+// it, and the cap bounds every wait: a grid that is not all resident, or a
+// launch on another stream sharing the counters, can cost time, never
+// correctness.  The counters are file-scope device arrays, zero at load;
+// each use of a slot brings its count back to zero.
+constexpr unsigned int kSoftPct = 90;
+constexpr uint64_t kSoftCapTicks = 20000;  // 200 us
+constexpr int kSoftSlots = 64;
+__device__ unsigned int g_soft_arrive[kSoftSlots];
+__device__ unsigned int g_soft_gen[kSoftSlots];
+
+// Barrier number j of a launch (j >= 1); every thread of the workgroup calls it.
+__device__ __forceinline__ void soft_barrier(int j) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int s = j & (kSoftSlots - 1);
+    const unsigned int g = gridDim.x;
+    const unsigned int gen0 =
+        __hip_atomic_load(&g_soft_gen[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned int old =
+        __hip_atomic_fetch_add(&g_soft_arrive[s], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old + 1 >= g) {  // the last arrival: reset the slot, release the waiters
+      __hip_atomic_store(&g_soft_arrive[s], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(&g_soft_gen[s], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      const unsigned int enough = (g * kSoftPct) / 100;
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while (__hip_atomic_load(&g_soft_gen[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                 gen0 &&
+             __hip_atomic_load(&g_soft_arrive[s], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
+                 enough) {
+        __builtin_amdgcn_s_sleep(4);
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kSoftCapTicks) break;
+      }
+    }
+  }
+  __syncthreads();
+}
 constexpr int64_t kGroup = static_cast<int64_t>(kBlock) * kVec;  // elements per group
 
 template <int DT>

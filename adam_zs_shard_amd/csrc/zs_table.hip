@@ -2,28 +2,23 @@
 
 #include "zs_device.h"
 
-#include <hip/hip_cooperative_groups.h>
-
 namespace zs {
 namespace {
 
-// Rounds of entries between two grid-wide barriers (SYNC > 0, cooperative
-// launches only).  With one workgroup per CU the CUs drift out of step over
-// the rounds, until about a third of them read gradients while the rest
-// update, a mix HBM serves more slowly than either phase; a barrier every
-// 12 rounds puts them back in step (8-rank Llama-3-8B shard, 69 rounds:
-// 7.83 -> 7.73 ms; every 8 or 10 rounds about the same, every round or two
-// slower than none).
-constexpr int kTableSyncRounds = 12;
+// Rounds of entries between soft barriers (8-rank Llama-3-8B shard, 69
+// rounds: every 4, 5, 6 or 8 rounds 7.544 / 7.533 / 7.537 / 7.558 ms against
+// 7.826 with none and 7.715 with a full grid-wide barrier every 12 rounds;
+// every round 8.06).
+constexpr int kTableSoftRounds = 6;
 
 // Multi-tensor fused step, one workgroup per CU, one wave per SIMD: for each
 // chunk-table entry, the whole chunks of the entry, then its rest, by the
-// block that took the entry.  Entries go round-robin in rounds of gridDim.x;
-// SYNC > 0 adds a grid-wide barrier every SYNC rounds (every block takes the
-// same number of barriers, with or without an entry in the round).  The body
-// is the single-tensor kernel's (see fused_kernel for why it is written out
-// rather than factored).
-template <int GDT, int PDT, int FORM, int SYNC = 0>
+// block that took the entry.  Entries go round-robin in rounds of gridDim.x,
+// with a soft barrier every kTableSoftRounds rounds (every block takes it,
+// with or without an entry in the round).  The body is the single-tensor
+// kernel's (see fused_kernel for why it is written out rather than
+// factored).
+template <int GDT, int PDT, int FORM>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void table_kernel(TableSrc src, int p, Consts c0, const StepTableDev* st) {
   // The step's constants: by value, or the step table's current entry
@@ -42,9 +37,8 @@ void table_kernel(TableSrc src, int p, Consts c0, const StepTableDev* st) {
   constexpr int64_t kFull = static_cast<int64_t>(kBlock) * kGroupsMax;
   const int64_t nrounds = (src.count() + src.stride() - 1) / src.stride();
   for (int64_t rd = 0; rd < nrounds; ++rd) {
-    if constexpr (SYNC > 0) {
-      if (rd > 0 && rd % SYNC == 0) cooperative_groups::this_grid().sync();
-    }
+    if (rd > 0 && rd % kTableSoftRounds == 0)
+      soft_barrier(static_cast<int>(rd / kTableSoftRounds));
     const int64_t item = src.first() + rd * src.stride();
     if (item >= src.count()) continue;
     const auto R = src.open(item);
@@ -197,40 +191,16 @@ hipError_t launch_multi(const MultiLaunch& a) {
     });
     return hipGetLastError();
   }
-  // Long tables take the cooperative launch with barriers; a captured stream,
-  // a step table (launches meant for graphs) or a refused cooperative launch
-  // take the plain one.  Both give the same results.
-  const int64_t nrounds = (a.nchunks + grid - 1) / grid;
-  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-  const bool sync = a.steps == nullptr && nrounds >= 2 * kTableSyncRounds &&
-                    hipStreamIsCapturing(a.stream, &cap) == hipSuccess &&
-                    cap == hipStreamCaptureStatusNone;
-  hipError_t err = hipSuccess;
   with_dt(a.gdt, [&](auto G) {
     with_dt(a.pdt, [&](auto H) {
       with_form(a.form, [&](auto F) {
-        constexpr int GDT = decltype(G)::value, PDT = decltype(H)::value;
-        constexpr int FORM = decltype(F)::value;
-        if (sync) {
-          TableSrc s2 = src;
-          int p = a.p;
-          Consts c = a.c;
-          const StepTableDev* none = nullptr;
-          void* args[] = {&s2, &p, &c, &none};
-          err = hipLaunchCooperativeKernel(
-              reinterpret_cast<const void*>(table_kernel<GDT, PDT, FORM, kTableSyncRounds>),
-              dim3(static_cast<unsigned>(grid)), dim3(kBlock), args, 0, a.stream);
-          if (err == hipSuccess) return;
-          (void)hipGetLastError();  // refused: the plain launch below
-        }
-        table_kernel<GDT, PDT, FORM>
+        table_kernel<decltype(G)::value, decltype(H)::value, decltype(F)::value>
             <<<dim3(static_cast<unsigned>(grid)), dim3(kBlock), 0, a.stream>>>(src, a.p, a.c,
                                                                               a.steps);
-        err = hipGetLastError();
       });
     });
   });
-  return err;
+  return hipGetLastError();
 }
 
 }  // namespace zs

@@ -203,40 +203,43 @@ def test_gpt2_small_shapes_remaining_shards(k, npieces):
     _run_and_check(case, 2, 70 + k)
 
 
-def test_grid_barrier_launch_equals_plain_launch():
+def test_table_across_soft_barriers_by_value_and_step_table():
     # A table of 24 rounds of whole chunks (one 57,344-element entry per CU
-    # and round) takes the cooperative launch with grid-wide barriers when the
-    # constants come by value; through a step table it takes the plain
-    # launch.  Same inputs, same state: the two must agree bit for bit, and
-    # sampled elements must match the oracle.
+    # and round) passes three soft barriers per launch.  Launched with its
+    # constants by value and through a step table, from the same inputs and
+    # state, the two must agree bit for bit, and sampled elements (every
+    # round's first and last chunks, around the barriers) must match the
+    # oracle.
     ncu = torch.cuda.get_device_properties(0).multi_processor_count
     chunk = 28 * 256 * 8
     p = 2
     L = 24 * ncu * chunk + 12_345            # 24 full rounds and a ragged tail
     numel = [L * p]
-    say(f"grid-barrier table: {L} elements per shard, {24 * ncu} whole chunks")
+    say(f"soft-barrier table: {L} elements per shard, {24 * ncu} whole chunks")
     cases = [MtCase(numel, p, 1, "bf16", "bf16", chunk, 81) for _ in range(2)]
     assert cases[0].nchunks >= 24 * ncu
     for c in cases:
         c.set_grads(1, 82)
     hp = z.hparams(LR, B1, B2, EPS, 1)
-    z.zs_fused_shard_step_multi(cases[0].table, hp)                     # cooperative
+    z.zs_fused_shard_step_multi(cases[0].table, hp)
     nb = z.zs_step_table_bytes(1)
     stdev = torch.empty(nb, dtype=torch.uint8, device=DEV)
     steps = z.zs_step_table_init(hp, p, 1, stdev, nb)
-    z.zs_fused_shard_step_multi_dev(cases[1].table, steps)              # plain
+    z.zs_fused_shard_step_multi_dev(cases[1].table, steps)
     torch.cuda.synchronize()
     for name in ("w", "m", "v"):
         a, b = getattr(cases[0], name), getattr(cases[1], name)
         assert torch.equal(a.view(torch.int32), b.view(torch.int32)), name
     pa, pb = cases[0].params[0], cases[1].params[0]
     assert torch.equal(pa.view(torch.int16), pb.view(torch.int16))
-    # oracle on sampled elements of the shard (every CU's first and last chunk
-    # of the first and last rounds, and the tail)
+    # oracle on sampled elements of the shard: the first and last chunks of
+    # the first round, rounds 5-7 around the first barrier, the last round and
+    # the tail
     c0 = cases[0]
     idx = np.unique(np.concatenate([
         np.arange(0, 64), np.arange(chunk - 64, chunk + 64),
         np.arange((ncu - 1) * chunk, ncu * chunk, 997),
+        np.arange(5 * ncu * chunk, 8 * ncu * chunk, 7919),
         np.arange(23 * ncu * chunk, 23 * ncu * chunk + 4096, 13),
         np.arange(L - 12_345, L)]))
     gb = [g[idx] for g in c0.gbits]
@@ -251,11 +254,11 @@ def test_grid_barrier_launch_equals_plain_launch():
     assert d == 0
 
 
-def test_long_table_captured_by_value_takes_plain_launch():
-    # The same 24-round table with its constants by value, launched on a
-    # stream under capture: the launcher must not try the cooperative launch
-    # there.  Two replays of the graph must equal two eager (cooperative)
-    # launches of the same step on a copy with the same state.
+def test_long_table_graph_replays_equal_eager_launches():
+    # The same 24-round table with its constants by value, captured in a HIP
+    # graph: its soft-barrier counters need no clearing between launches, so
+    # two replays must equal two eager launches of the same step on a copy
+    # with the same state.
     ncu = torch.cuda.get_device_properties(0).multi_processor_count
     chunk = 28 * 256 * 8
     p = 2
@@ -284,3 +287,32 @@ def test_long_table_captured_by_value_takes_plain_launch():
             a, b = getattr(eager, name), getattr(graphed, name)
             assert torch.equal(a.view(torch.int32), b.view(torch.int32)), (rep, name)
         assert torch.equal(eager.params[0].view(torch.int16), graphed.params[0].view(torch.int16)), rep
+
+
+def test_concurrent_tables_share_soft_barriers():
+    # Two 12-round tables (two soft barriers each) stepped at once on two
+    # streams share the soft-barrier counters, which only pace the
+    # workgroups: each result must equal the same table stepped alone.
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    chunk = 28 * 256 * 8
+    p = 2
+    L = 12 * ncu * chunk + 4321
+    say(f"two concurrent tables: {L} elements per shard")
+    alone = [MtCase([L * p], p, 1, "bf16", "bf16", chunk, 85 + i) for i in range(2)]
+    together = [MtCase([L * p], p, 1, "bf16", "bf16", chunk, 85 + i) for i in range(2)]
+    for i, c in enumerate(alone + together):
+        c.set_grads(1, 90 + i % 2)
+    hp = z.hparams(LR, B1, B2, EPS, 1)
+    for c in alone:
+        z.zs_fused_shard_step_multi(c.table, hp)
+        torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in together]
+    for s_ in streams:
+        s_.wait_stream(torch.cuda.current_stream())
+    for c, s_ in zip(together, streams):
+        z.zs_fused_shard_step_multi(c.table, hp, stream=s_.cuda_stream)
+    torch.cuda.synchronize()
+    for a, b in zip(alone, together):
+        for name in ("w", "m", "v"):
+            assert torch.equal(getattr(a, name).view(torch.int32), getattr(b, name).view(torch.int32)), name
+        assert torch.equal(a.params[0].view(torch.int16), b.params[0].view(torch.int16))

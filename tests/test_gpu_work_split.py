@@ -86,8 +86,8 @@ def test_work_split_heads_and_tails(tail, offset):
 
 @pytest.mark.parametrize("p", [1, 5, 19])
 def test_small_shard_kernel(p):
-    # just under half a whole chunk per CU: the small-shard kernel (four
-    # workgroups per CU, ranks in batches of at most 8: 19 = 8 + 8 + 2 + 1)
+    # just under half a whole chunk per CU: the small-shard kernel (three
+    # workgroups per CU, ranks in batches of 4: 19 = 4 + 4 + 4 + 4 + 3)
     cu = _cu()
     L = (cu // 2 - 1) * CHUNK + 8 * 77 + 3
     say(f"small-shard kernel: L={L}, p={p} on {cu} CUs")
@@ -103,3 +103,49 @@ def test_whole_chunks_beyond_64_ranks(p):
     L = (cu // 2 + 1) * CHUNK + 8 * 21 + 3
     say(f"whole chunks at {p} ranks: L={L} on {cu} CUs")
     _run(L, p, "f16", 1, seed_for(63, p), offset=1)
+
+
+def test_rounds_across_soft_barriers():
+    # four rounds of whole chunks (the last half full) take one soft barrier,
+    # after the third round; every element against the oracle
+    cu = _cu()
+    L = (3 * cu + cu // 2) * CHUNK + 8 * 37 + 6
+    say(f"rounds across a soft barrier: L={L} on {cu} CUs")
+    _run(L, 2, "f16", 1, seed_for(64, 1), offset=2)
+
+
+def test_concurrent_steps_share_soft_barriers():
+    # Two shards stepped at once on two streams share the soft-barrier
+    # counters (they only pace the workgroups): each result must equal the
+    # same step run alone.
+    cu = _cu()
+    L = 7 * cu * CHUNK + 8 * 3 + 1          # seven rounds: two barriers
+    n, p = 2 * L, 2
+    say(f"two concurrent shard steps: L={L} on {cu} CUs")
+    runs = []
+    for i in range(2):
+        g = [normal(L, 1e-3, seed_for(65, i, r), torch.float16).to(DEV) for r in range(p)]
+        w0 = normal(L, 0.02, seed_for(65, i, 9)).to(DEV)
+        runs.append([g, w0])
+    def state(w0):
+        return [w0.clone(), torch.zeros_like(w0), torch.zeros_like(w0),
+                torch.zeros(L, dtype=torch.float16, device=DEV)]
+    hp = z.hparams(LR, B1, B2, EPS, 1)
+    alone = []
+    for g, w0 in runs:
+        st = state(w0)
+        z.zs_fused_shard_step(n, p, 0, g, *st, hp, grad_base=0, param_base=0)
+        torch.cuda.synchronize()
+        alone.append(st)
+    together = [state(w0) for _, w0 in runs]
+    streams = [torch.cuda.Stream() for _ in runs]
+    for s_ in streams:
+        s_.wait_stream(torch.cuda.current_stream())
+    for (g, _), st, s_ in zip(runs, together, streams):
+        z.zs_fused_shard_step(n, p, 0, g, *st, hp, grad_base=0, param_base=0,
+                              stream=s_.cuda_stream)
+    torch.cuda.synchronize()
+    for a, b in zip(alone, together):
+        for x, y in zip(a[:3], b[:3]):
+            assert torch.equal(x.view(torch.int32), y.view(torch.int32))
+        assert torch.equal(a[3].view(torch.int16), b[3].view(torch.int16))
