@@ -161,9 +161,9 @@ hipError_t launch_rank_table(const uint16_t* const* src, int n, const uint16_t**
 // cursor += 1 in a step table, one thread.
 hipError_t launch_step_advance(StepTableDev* t, hipStream_t stream);
 
-// Elements (0..7) to peel before the first 8-element group so that as many
-// of the given 16-bit (a16) and fp32 (a32) streams as possible start their
-// groups on 16-byte boundaries.
+// Elements (0..7) to peel before the first 8-element group so that the
+// given 16-bit (a16) and fp32 (a32) streams, weighted by their bytes, start
+// their groups as close to whole 128-byte lines as possible.
 int choose_head(const std::vector<uintptr_t>& a16, const std::vector<uintptr_t>& a32);
 
 // Bytes of the library's static device scratch (one copy per GPU): the rank
