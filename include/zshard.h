@@ -33,10 +33,16 @@
  *    Host memory the call needs for its own bookkeeping that cannot be had
  *    gives ZS_ERR_RESOURCE (no exception crosses this interface).
  *  - Shards that are empty (s_k == e_k) return ZS_OK without launching.
- *  - No alignment is required.  Arrays whose addresses line up on 16 bytes
- *    at a common element take the widest loads.
+ *  - No alignment is required.  The kernels run fastest when the arrays'
+ *    element 0 sits on a 128-byte line (or all sit the same distance into
+ *    one); the call peels 0-7 leading elements to line up as many of the
+ *    arrays' bytes as it can.
  *  - The functions are re-entrant; concurrent calls on one stream run in
  *    order, calls on different streams must not write the same memory.
+ *    The whole-chunk kernels pace their workgroups through small device
+ *    counters shared by all calls on a GPU; calls overlapping on different
+ *    streams may slow each other there, never change each other's
+ *    results.
  *  - Numerics: every fp32 constant is computed in double and rounded once;
  *    the mean is an fp32 left fold in rank order; no operation is fused
  *    (no FMA contraction); division and square root are correctly rounded;
