@@ -176,3 +176,45 @@ def test_adam_step_whole_chunk_path(with_param, off):
         canary = u16(pbuf)
         assert not canary[:off].any() and not canary[off + L:].any(), "write outside the shard"
     assert d == 0
+
+
+@pytest.mark.parametrize("case", range(10))
+def test_adam_step_alignment_sweep(case):
+    # every array at its own element offset within a 128-byte line (fp32:
+    # 0-31 elements, the 16-bit working copy: 0-63): the head (0-7 scalar
+    # elements) follows the alignment; every element must match the oracle.
+    # Cases 8 and 9 take the whole-chunk kernel with the state on whole lines
+    # and the working copy 40 / 8 bytes into one (rank 63's slice of the
+    # 7.5B-parameter working copy sits 40 bytes in).
+    rng = np.random.default_rng(100 + case)
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    if case < 8:
+        L = 50_021 + case * 997
+        go, wo, mo, vo = (int(x) for x in rng.integers(0, 32, 4))
+        po = int(rng.integers(0, 64))
+    else:
+        L = (cu // 2 + 3) * 28 * 256 * 8 + 8 * 29 + 3
+        go = wo = mo = vo = 0
+        po = 20 if case == 8 else 4
+    g = normal(L, 1e-2, seed_for(44, case)).numpy()
+    w0 = normal(L, 0.02, seed_for(45, case)).numpy()
+    m0, v0 = (x.numpy() for x in make.random_state(L, 46 + case))
+
+    def dev(x, off):
+        buf = torch.zeros(L + 32, dtype=torch.float32, device=DEV)
+        assert buf.data_ptr() % 128 == 0
+        buf[off:off + L].copy_(torch.from_numpy(x))
+        return buf[off:off + L]
+
+    gd, wd, md, vd = dev(g, go), dev(w0, wo), dev(m0, mo), dev(v0, vo)
+    pbuf = torch.zeros(L + 64, dtype=torch.float16, device=DEV)
+    par = pbuf[po:po + L]
+    z.zs_adam_step(gd, wd, md, vd, par, L, z.hparams(LR, B1, B2, EPS, 3))
+    torch.cuda.synchronize()
+    wh, mh, vh = w0.copy(), m0.copy(), v0.copy()
+    ph = oracle.adam_apply(g, wh, mh, vh, "f16", LR, B1, B2, EPS, 3)
+    d = check_f32(f32(wd), wh, 2e-6, "w") + check_f32(f32(md), mh, 2e-6, "m")
+    d += check_f32(f32(vd), vh, 2e-6, "v") + check_param(u16(par), ph, "f16", "param")
+    assert d == 0
+    canary = u16(pbuf)
+    assert not canary[:po].any() and not canary[po + L:].any(), "write outside the slice"
