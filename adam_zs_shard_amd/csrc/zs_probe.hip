@@ -16,6 +16,7 @@
 #include <stdint.h>
 
 #include "../../include/zsprobe.h"
+#include "zs_device.h"  // zs::soft_barrier, the library's pacing of whole-chunk rounds
 
 namespace {
 
@@ -166,12 +167,21 @@ __device__ __forceinline__ void add8(float (&a)[8], const u32x4& q) {
   }
 }
 
+// PACED: rounds of one chunk per workgroup with the library's soft barrier
+// every `pace` rounds; otherwise plain grid-stride over the chunks.
+template <bool PACED>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void step_reads_kernel(StepRanks R, int p, int64_t nchunks, u32x4* __restrict__ sink) {
+void step_reads_kernel(StepRanks R, int p, int64_t nchunks, int pace, u32x4* __restrict__ sink) {
   const uint32_t off = threadIdx.x * 16u;
   constexpr int64_t kChunk = static_cast<int64_t>(kStepGroups) * kBlock * 8;  // elements
   float keep = 0.0f;
-  for (int64_t ch = blockIdx.x; ch < nchunks; ch += gridDim.x) {
+  const int64_t nrounds = (nchunks + gridDim.x - 1) / gridDim.x;
+  for (int64_t rd = 0; rd < nrounds; ++rd) {
+    if constexpr (PACED) {
+      if (rd > 0 && rd % pace == 0) zs::soft_barrier(static_cast<int>(rd / pace));
+    }
+    const int64_t ch = blockIdx.x + rd * gridDim.x;
+    if (ch >= nchunks) continue;
     float s[kStepGroups][8];
 #pragma unroll
     for (int u = 0; u < kStepGroups; ++u)
@@ -252,18 +262,35 @@ int32_t zsp_stream(int32_t mix, const void* src, void* dst, int64_t stream_bytes
   return e == hipSuccess ? 0 : 2;
 }
 
-int32_t zsp_step_reads(const void* const* ranks, int32_t p, int64_t elems, int32_t grid,
-                       void* sink, void* stream) {
-  if (!ranks || !sink || p < 1 || p > kStepRanks || elems < 0 || grid < 1) return 1;
+static int32_t step_reads(const void* const* ranks, int32_t p, int64_t elems, int32_t grid,
+                          int32_t pace, void* sink, void* stream) {
+  if (!ranks || !sink || p < 1 || p > kStepRanks || elems < 0 || grid < 1 || pace < 0)
+    return 1;
   StepRanks R;
   for (int r = 0; r < kStepRanks; ++r) {
     R.g[r] = r < p ? static_cast<const uint16_t*>(ranks[r]) : nullptr;
     if (r < p && !R.g[r]) return 1;
   }
   const int64_t nchunks = elems / (static_cast<int64_t>(kStepGroups) * kBlock * 8);
-  step_reads_kernel<<<dim3(grid), dim3(kBlock), 0, static_cast<hipStream_t>(stream)>>>(
-      R, p, nchunks, static_cast<u32x4*>(sink));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (pace > 0)
+    step_reads_kernel<true><<<dim3(grid), dim3(kBlock), 0, s>>>(R, p, nchunks, pace,
+                                                              static_cast<u32x4*>(sink));
+  else
+    step_reads_kernel<false><<<dim3(grid), dim3(kBlock), 0, s>>>(R, p, nchunks, 1,
+                                                               static_cast<u32x4*>(sink));
   return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+int32_t zsp_step_reads(const void* const* ranks, int32_t p, int64_t elems, int32_t grid,
+                       void* sink, void* stream) {
+  return step_reads(ranks, p, elems, grid, 0, sink, stream);
+}
+
+int32_t zsp_step_reads_paced(const void* const* ranks, int32_t p, int64_t elems, int32_t grid,
+                             int32_t pace_rounds, void* sink, void* stream) {
+  if (pace_rounds < 1) return 1;
+  return step_reads(ranks, p, elems, grid, pace_rounds, sink, stream);
 }
 
 int32_t zsp_streams(int32_t mix, int32_t* nread, int32_t* nwrite) {

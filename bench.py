@@ -679,28 +679,38 @@ def ceiling(args):
     chunk = 28 * 256 * 8
     moved = (M // chunk) * chunk * 2 * wl.p
 
-    def launch_reads():
-        rc = P.zsp_step_reads(arr, wl.p, M, ncu, sink.data_ptr(), stream.cuda_stream)
-        assert rc == 0, f"probe step_reads failed ({rc})"
+    P.zsp_step_reads_paced.argtypes = [C.POINTER(C.c_void_p), C.c_int32, C.c_int64, C.c_int32,
+                                       C.c_int32, C.c_void_p, C.c_void_p]
+    P.zsp_step_reads_paced.restype = C.c_int32
+    # plain, and paced like the library's whole-chunk kernels (a soft barrier
+    # every 2 rounds, the pacing of its read-only mean kernel)
+    for name, pace in (("step_reads_p64", 0), ("step_reads_p64_paced", 2)):
+        def launch_reads(pace=pace):
+            if pace:
+                rc = P.zsp_step_reads_paced(arr, wl.p, M, ncu, pace, sink.data_ptr(),
+                                            stream.cuda_stream)
+            else:
+                rc = P.zsp_step_reads(arr, wl.p, M, ncu, sink.data_ptr(), stream.cuda_stream)
+            assert rc == 0, f"probe {name} failed ({rc})"
 
-    for _ in range(2):
-        launch_reads()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(10):
-        launch_reads()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / 10
-    gbs = moved / (ms / 1e3) / 1e9
-    out["step_reads_p64"] = {"streams_read": wl.p, "streams_written": 0, "bytes_per_launch": moved,
-                             "best_gbs": round(gbs, 1), "best_frac_of_8tbs": round(gbs / HBM_PEAK_GBS, 4),
-                             "best_workgroups_per_cu": 1, "best_ms": round(ms, 4),
-                             "gbs_by_workgroups_per_cu": {"1_per_cu": round(gbs, 1)},
-                             "step_bytes_per_element": None}
-    print(f"[ceiling] step_reads_p64: {gbs:.0f} GB/s ({ms:.3f} ms)", file=sys.stderr, flush=True)
+        for _ in range(2):
+            launch_reads()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            launch_reads()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 10
+        gbs = moved / (ms / 1e3) / 1e9
+        out[name] = {"streams_read": wl.p, "streams_written": 0, "bytes_per_launch": moved,
+                     "best_gbs": round(gbs, 1), "best_frac_of_8tbs": round(gbs / HBM_PEAK_GBS, 4),
+                     "best_workgroups_per_cu": 1, "best_ms": round(ms, 4),
+                     "gbs_by_workgroups_per_cu": {"1_per_cu": round(gbs, 1)},
+                     "step_bytes_per_element": None, "soft_barrier_every_rounds": pace or None}
+        print(f"[ceiling] {name}: {gbs:.0f} GB/s ({ms:.3f} ms)", file=sys.stderr, flush=True)
     del ranks
     torch.cuda.empty_cache()
     print(json.dumps({"ceiling": out, "peak_gbs": HBM_PEAK_GBS, "cus": ncu}), flush=True)

@@ -60,6 +60,14 @@ int32_t zsp_stream(int32_t mix, const void* src, void* dst, int64_t stream_bytes
 int32_t zsp_step_reads(const void* const* ranks, int32_t p, int64_t elems, int32_t grid,
                        void* sink, void* stream);
 
+/* The same read phase paced like the library's whole-chunk kernels: the
+ * chunks go in rounds of one per workgroup, and every `pace_rounds` rounds
+ * (>= 1) each workgroup passes the library's soft barrier (it waits until
+ * 90% of the grid has arrived, at most 200 us).  Same arguments and
+ * returns as zsp_step_reads; pace_rounds < 1 returns 1. */
+int32_t zsp_step_reads_paced(const void* const* ranks, int32_t p, int64_t elems, int32_t grid,
+                             int32_t pace_rounds, void* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,7 +30,7 @@ def probe():
 def test_exports_every_declared_function(probe):
     text = open(os.path.join(ROOT, "include", "zsprobe.h")).read()
     names = re.findall(r"^int32_t (\w+)\(", text, re.M)
-    assert sorted(names) == ["zsp_step_reads", "zsp_stream", "zsp_streams"]
+    assert sorted(names) == ["zsp_step_reads", "zsp_step_reads_paced", "zsp_stream", "zsp_streams"]
     for n in names:
         assert hasattr(probe, n), n
 
@@ -77,3 +77,9 @@ def test_bad_arguments_launch_nothing(probe):
     assert probe.zsp_step_reads(ranks, 8, 1 << 20, 256, None, None) == 1            # no sink
     holes = (C.c_void_p * 8)(*([fake] * 7 + [None]))
     assert probe.zsp_step_reads(holes, 8, 1 << 20, 256, fake, None) == 1            # a null rank
+    probe.zsp_step_reads_paced.argtypes = [C.POINTER(C.c_void_p), C.c_int32, C.c_int64,
+                                           C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]
+    probe.zsp_step_reads_paced.restype = C.c_int32
+    assert probe.zsp_step_reads_paced(ranks, 8, 1 << 20, 256, 0, fake, None) == 1   # pace < 1
+    assert probe.zsp_step_reads_paced(ranks, 65, 1 << 20, 256, 2, fake, None) == 1  # p > 64
+    assert probe.zsp_step_reads_paced(holes, 8, 1 << 20, 256, 2, fake, None) == 1   # a null rank
