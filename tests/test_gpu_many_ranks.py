@@ -183,3 +183,66 @@ def test_mean16_whole_chunks_bit_exact():
     want = oracle.narrow("bf16", oracle.grad_mean("bf16", [u16(g) for g in gd]))
     torch.cuda.synchronize()
     assert np.array_equal(u16(out), want)
+
+
+def test_fused_step_1024_ranks_across_soft_barriers_sampled():
+    # 1024 ranks (pointers from the device workspace), seven rounds of whole
+    # chunks on every CU (soft barriers before rounds 3 and 6), then pieces
+    # and a ragged tail.  Rank r reads buffer r % 16 (inputs may share
+    # memory), which keeps 16 x L values instead of 1024 x L.
+    p, k, nbuf = 1024, 1023, 16
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    L = 7 * ncu * CHUNK + 5 * GROUP + 11
+    n = L * p
+    M, s, e = oracle.plan_shards(n, p)
+    assert e[k] - s[k] == L
+    say(f"1024 ranks over {nbuf} buffers, shard {k}: {L} elements")
+    bufs = _grads_dev(nbuf, L, "f16", 68, std=1e-3)
+    gd = [bufs[r % nbuf] for r in range(p)]
+    w0 = normal(L, 0.02, seed_for(69)).to(DEV)
+    wd = w0.clone()
+    md, vd = torch.zeros_like(wd), torch.zeros_like(wd)
+    param_d = torch.empty(L, dtype=torch.float16, device=DEV)
+    ws = torch.empty(z.zs_shard_workspace_bytes(p), dtype=torch.uint8, device=DEV)
+    z.zs_fused_shard_step(n, p, k, gd, wd, md, vd, param_d, z.hparams(LR, B1, B2, EPS, 1),
+                          grad_base=s[k], param_base=s[k], workspace=ws)
+    idx = np.unique(np.concatenate([
+        _sample(L, 6_000, 70),
+        np.arange(3 * ncu * CHUNK - 64, 3 * ncu * CHUNK + 64),      # around the first barrier
+        np.arange(6 * ncu * CHUNK - 64, 6 * ncu * CHUNK + 64)]))    # and the second
+    idev = torch.from_numpy(idx).to(DEV)
+    bs = [u16(b[idev]) for b in bufs]
+    gs = [bs[r % nbuf] for r in range(p)]
+    wh = f32(w0[idev]).copy()
+    mh, vh = np.zeros(idx.size, np.float32), np.zeros(idx.size, np.float32)
+    ph = oracle.step_elems("f16", gs, wh, mh, vh, "f16", LR, B1, B2, EPS, 1)
+    torch.cuda.synchronize()
+    d = check_f32(f32(wd[idev]), wh, 1e-6, "w") + check_f32(f32(md[idev]), mh, 1e-6, "m")
+    d += check_f32(f32(vd[idev]), vh, 1e-6, "v")
+    d += check_param(u16(param_d[idev]), ph, "f16", "param")
+    assert d == 0, f"{d} sampled values differ in bits"
+    assert torch.equal(param_d.view(torch.int16), wd.to(torch.float16).view(torch.int16))
+
+
+def test_mean_in_passes_across_soft_barriers_sampled():
+    # 300 ranks: two passes (256 + 44 ranks), each over five rounds of whole
+    # chunks (soft barriers before rounds 2 and 4); rank r reads buffer r % 12
+    p, k, nbuf = 300, 299, 12
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    L = 5 * ncu * CHUNK + 3 * GROUP + 7
+    n = L * p
+    M, s, e = oracle.plan_shards(n, p)
+    say(f"300-rank mean over {nbuf} buffers: {L} elements")
+    bufs = _grads_dev(nbuf, L, "bf16", 71)
+    gd = [bufs[r % nbuf] for r in range(p)]
+    out = torch.empty(L, device=DEV)
+    z.zs_reduce_scatter_mean_local(gd, n, p, k, out, grad_base=s[k])
+    idx = np.unique(np.concatenate([
+        _sample(L, 6_000, 72),
+        np.arange(2 * ncu * CHUNK - 64, 2 * ncu * CHUNK + 64),
+        np.arange(4 * ncu * CHUNK - 64, 4 * ncu * CHUNK + 64)]))
+    idev = torch.from_numpy(idx).to(DEV)
+    bs = [u16(b[idev]) for b in bufs]
+    want = oracle.grad_mean("bf16", [bs[r % nbuf] for r in range(p)])
+    torch.cuda.synchronize()
+    assert np.array_equal(f32(out[idev]).view(np.uint32), want.view(np.uint32))
