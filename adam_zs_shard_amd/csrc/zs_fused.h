@@ -8,57 +8,6 @@
 namespace zs {
 namespace {
 
-// Staging of the 16-bit working copy (Adam forms).  A shard's slice of the
-// full working copy starts wherever s_k puts it (rank 63 of the 7.5B shard:
-// 40 bytes into a 64-byte segment), so each wave's 1 KiB of stores would
-// begin and end mid-line.  Instead each lane puts its 16 bytes of every
-// group into LDS at their place relative to the 128-byte line below the
-// chunk's start (rounded down to 8 bytes: two 8-byte LDS writes), and after
-// the chunk's update the workgroup writes the chunk's 112 KiB out in 16-byte
-// units on whole lines; only the two lines at the chunk's ends are partial
-// (7.5B shard: 2.674 -> 2.651 ms in one process).
-typedef uint32_t u32x4a16 __attribute__((ext_vector_type(4), aligned(16)));
-typedef uint32_t u32x2a8 __attribute__((ext_vector_type(2), aligned(8)));
-constexpr uint32_t kChunkCopyBytes = kGroupsMax * kBlock * kVec * 2;  // 114,688
-constexpr uint32_t kCopyStage = kChunkCopyBytes + 128;
-
-// The lane's 8 values of group u; y = u * 4096 + 16 * lane + (offset in the line & ~7).
-__device__ __forceinline__ void stage_copy(unsigned char* lds, uint32_t y, u32x4 x) {
-  reinterpret_cast<u32x2a8*>(lds + y)[0] = u32x2a8{x[0], x[1]};
-  reinterpret_cast<u32x2a8*>(lds + y)[1] = u32x2a8{x[2], x[3]};
-}
-
-// The staged chunk out to bytes [a0 + d, a0 + d + kChunkCopyBytes), a0 on a
-// 128-byte line; LDS byte y holds byte a0 + (d & 7) + y.
-__device__ __forceinline__ void flush_copy(const unsigned char* lds, unsigned char* a0,
-                                           uint32_t d) {
-  const uint32_t r = d & 7u;
-  const uint32_t end = d + kChunkCopyBytes;
-  const uint32_t nunits = (end + 15u) / 16u;
-  for (uint32_t i = threadIdx.x; i < nunits; i += kBlock) {
-    const uint32_t b = 16u * i;
-    if (b >= d && b + 16u <= end) {
-      u32x4a16 x;
-      if (r == 0) {
-        x = *reinterpret_cast<const u32x4a16*>(lds + b);
-      } else {
-        const uint16_t* q = reinterpret_cast<const uint16_t*>(lds + b - r);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) x[j] = q[2 * j] | (static_cast<uint32_t>(q[2 * j + 1]) << 16);
-      }
-      __builtin_nontemporal_store(x, reinterpret_cast<u32x4a16*>(a0 + b));
-    } else {
-#pragma unroll
-      for (uint32_t j = 0; j < 16u; j += 2u) {
-        const uint32_t bj = b + j;
-        if (bj >= d && bj < end)
-          *reinterpret_cast<uint16_t*>(a0 + bj) =
-              *reinterpret_cast<const uint16_t*>(lds + bj - r);
-      }
-    }
-  }
-}
-
 // Rounds of chunks between soft barriers (117M-element, 64-rank shard, 8
 // rounds: every 2, 3 or 4 rounds 2.686 / 2.683 / 2.692 ms against 2.723 with
 // none; every round no gain).

@@ -311,6 +311,36 @@ __device__ __forceinline__ void adam_group(const Consts& c, const Lanes& L, cons
   apply_group<PDT, FORM, false, PARAM>(c, L, q, g, w, m, v, par, e0);
 }
 
+// adam_group with the working copy staged in LDS (stage_quad) instead of
+// stored: the quads go to y and y + 512.
+template <int PDT, int FORM>
+__device__ __forceinline__ void adam_group_staged(const Consts& c, const Lanes& L,
+                                                  const float* gin, float* w, float* m, float* v,
+                                                  int64_t e0, unsigned char* lds, uint32_t y) {
+  float g[kVec];
+  ld_f8(gin + e0, L, g);
+  const GroupState q = load_group<FORM>(L, w, m, v, e0);
+  float W[kVec] = {q.w0.x, q.w0.y, q.w0.z, q.w0.w, q.w1.x, q.w1.y, q.w1.z, q.w1.w};
+  float M[kVec] = {q.m0.x, q.m0.y, q.m0.z, q.m0.w, q.m1.x, q.m1.y, q.m1.z, q.m1.w};
+  float V[kVec] = {q.v0.x, q.v0.y, q.v0.z, q.v0.w, q.v1.x, q.v1.y, q.v1.z, q.v1.w};
+  if constexpr (FORM == kStandard || FORM == kPage1Literal) {
+    float MH[kVec], VH[kVec];
+    adam_moments8<FORM>(c, g, M, V, MH, VH);
+    st_f8(m + e0, L, M);
+    st_f8(v + e0, L, V);
+    __builtin_amdgcn_sched_barrier(0);  // the moments go out before the weight arithmetic
+    adam_weights8(c, MH, VH, W);
+    st_f8(w + e0, L, W);
+  } else {
+#pragma unroll
+    for (int j = 0; j < kVec; ++j) adam1<FORM>(c, g[j], W[j], M[j], V[j]);
+    st_f8(w + e0, L, W);
+    if constexpr (kUsesM<FORM>) st_f8(m + e0, L, M);
+  }
+  stage_quad(lds, y, u32x2{narrow2<PDT>(W[0], W[1]), narrow2<PDT>(W[2], W[3])});
+  stage_quad(lds, y + 512u, u32x2{narrow2<PDT>(W[4], W[5]), narrow2<PDT>(W[6], W[7])});
+}
+
 // Adam + downcast from a stored fp32 gradient, for smaller shards: pairs of
 // full groups grid-stride (both groups' loads in flight together), then the
 // odd full group and the partial group as two more items, then the scalars
@@ -362,12 +392,28 @@ void adam_chunk_kernel(const float* __restrict__ gin, float* __restrict__ w,
   const int64_t nvec = (len - h) / kVec;
   constexpr int64_t kFull = static_cast<int64_t>(kBlock) * kGroupsMax;
   const int64_t nfull = nvec / kFull;
+  __shared__ __attribute__((aligned(16))) unsigned char copy_lds[PARAM ? kCopyStage : 16];
   for (int64_t ch = blockIdx.x; ch < nfull; ch += gridDim.x) {
     const int64_t g0 = ch * kFull;
+    if constexpr (PARAM) {
+      // the chunk's working copy staged in LDS, written out on whole lines
+      unsigned char* const pc = reinterpret_cast<unsigned char*>(par + h + g0 * kVec);
+      const uint32_t dl = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(pc) & 127u);
+      const uint32_t ys = L.q16 + (dl & ~7u);
+      __syncthreads();  // the previous chunk's flush has read the staged copy
 #pragma unroll
-    for (int u = 0; u < kGroupsMax; ++u)
-      adam_group<PDT, FORM, PARAM>(c, L, gin, w, m, v, par,
-                                   h + (g0 + static_cast<int64_t>(u) * kBlock) * kVec);
+      for (int u = 0; u < kGroupsMax; ++u)
+        adam_group_staged<PDT, FORM>(c, L, gin, w, m, v,
+                                     h + (g0 + static_cast<int64_t>(u) * kBlock) * kVec,
+                                     copy_lds, static_cast<uint32_t>(u) * (kBlock * kVec * 2) + ys);
+      __syncthreads();
+      flush_copy(copy_lds, pc - dl, dl);
+    } else {
+#pragma unroll
+      for (int u = 0; u < kGroupsMax; ++u)
+        adam_group<PDT, FORM, PARAM>(c, L, gin, w, m, v, par,
+                                     h + (g0 + static_cast<int64_t>(u) * kBlock) * kVec);
+    }
   }
   const int64_t nfg = nvec / kBlock, part = nvec % kBlock;
   for (int64_t gi = nfull * kGroupsMax + blockIdx.x; gi < nfg; gi += gridDim.x)
