@@ -178,14 +178,16 @@ def test_adam_step_whole_chunk_path(with_param, off):
     assert d == 0
 
 
-@pytest.mark.parametrize("case", range(10))
+@pytest.mark.parametrize("case", range(12))
 def test_adam_step_alignment_sweep(case):
     # every array at its own element offset within a 128-byte line (fp32:
     # 0-31 elements, the 16-bit working copy: 0-63): the head (0-7 scalar
     # elements) follows the alignment; every element must match the oracle.
-    # Cases 8 and 9 take the whole-chunk kernel with the state on whole lines
-    # and the working copy 40 / 8 bytes into one (rank 63's slice of the
-    # 7.5B-parameter working copy sits 40 bytes in).
+    # Cases 8-11 take the whole-chunk kernel with the state on whole lines
+    # and the working copy 40 / 8 / 2 / 4 bytes into one (rank 63's slice of
+    # the 7.5B-parameter working copy sits 40 bytes in; the copy is staged in
+    # LDS and written out on whole lines, 2- and 4-byte offsets through the
+    # element-wise flush).
     rng = np.random.default_rng(100 + case)
     cu = torch.cuda.get_device_properties(0).multi_processor_count
     if case < 8:
@@ -195,7 +197,7 @@ def test_adam_step_alignment_sweep(case):
     else:
         L = (cu // 2 + 3) * 28 * 256 * 8 + 8 * 29 + 3
         go = wo = mo = vo = 0
-        po = 20 if case == 8 else 4
+        po = {8: 20, 9: 4, 10: 1, 11: 2}[case]
     g = normal(L, 1e-2, seed_for(44, case)).numpy()
     w0 = normal(L, 0.02, seed_for(45, case)).numpy()
     m0, v0 = (x.numpy() for x in make.random_state(L, 46 + case))
