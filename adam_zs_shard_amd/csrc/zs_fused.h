@@ -116,8 +116,10 @@ void fused_kernel(GradArgs<PMAX> ga, int p, float* __restrict__ w, float* __rest
     if constexpr (FORM == kStandard || FORM == kPage1Literal) {
       // Each group's Adam in two halves: the m and v stores go out after the
       // moments, then the next group's state loads, then the weight
-      // arithmetic and the w and working-copy stores, so the stores leave in
-      // two bursts and the next loads are in flight during the divisions.
+      // arithmetic and the w store, so the stores leave in two bursts and the
+      // next loads are in flight during the divisions.  The working copy goes
+      // to LDS (stage_copy) and out on whole lines after the chunk
+      // (flush_copy).
       const int64_t eb = h + g0 * kVec;
       unsigned char* const pc = reinterpret_cast<unsigned char*>(par + eb);
       const uint32_t dl = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(pc) & 127u);
