@@ -190,6 +190,7 @@ __device__ __forceinline__ void flush_copy(const unsigned char* lds, unsigned ch
     }
   }
 }
+
 constexpr int64_t kGroup = static_cast<int64_t>(kBlock) * kVec;  // elements per group
 
 template <int DT>
